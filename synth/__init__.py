@@ -1,0 +1,16 @@
+"""Seeded synthetic inputs for the MSA index-score operator.
+
+This package only draws and lays out input tensors (queries, paged or packed
+keys, int8 scales, block tables, sequence lengths).  It holds none of the
+operator's arithmetic, so both the CPU oracle's tests and the GPU path's tests
+and benchmark can use it without sharing any scoring code.
+"""
+from .inputs import (  # noqa: F401
+    MsaCase,
+    CONFIG_NAMES,
+    config_case,
+    make_case,
+    edge_cases,
+    poison_case,
+    case_summary,
+)

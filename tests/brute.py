@@ -1,0 +1,72 @@
+"""Vectorised brute force for the block score, used only to pin the oracle.
+
+It follows the block-selection sketch of the DSA forward-path notes (section
+3, "从 token score 得到 block Selection"): full token scores, ``masked_fill``
+of every invisible position with -inf, ``reshape`` into blocks of P tokens and
+``amax`` over each block; then the local_mask constants of the msa_index_score
+guide (section 二).  Inputs are decoded with torch's own ``.to(float64)`` and
+products are taken with torch matmul, so it shares nothing with the C oracle.
+"""
+import torch
+
+
+def _round16(n):
+    n = max(int(n), 1)
+    return (n + 15) // 16 * 16
+
+
+def request_keys(case, b):
+    """Dequantised keys k~ of request b as float64 [L, Hkv, D]."""
+    P = case.block_size
+    L = int(case.kv_len[b])
+    nb = -(-L // P)
+    if case.layout == "TND":
+        off = int(case.kv_len[:b].sum())
+        k = case.key[off:off + L].to(torch.float64)
+        s = case.scale[off:off + L].to(torch.float64) if case.scale is not None else None
+    else:
+        pages = case.block_table[b, :nb].long()
+        kp = case.key[pages].to(torch.float64)              # [nb, P, Hkv, D] or [nb, Hkv, P, D]
+        if case.layout == "BNBD":
+            kp = kp.permute(0, 2, 1, 3)
+        k = kp.reshape(nb * P, kp.shape[2], kp.shape[3])[:L]
+        s = None
+        if case.scale is not None:
+            s = case.scale[pages].to(torch.float64).permute(0, 2, 1).reshape(nb * P, -1)[:L]
+    if s is not None:
+        k = k * s[:, :, None]          # k~ = cast(k) * scale, exact in binary64
+    return k
+
+
+def brute_force(case) -> torch.Tensor:
+    P = case.block_size
+    Hq, T = case.Hq, case.T
+    W = _round16(case.max_blocks)
+    g = Hq // case.Hkv
+    out = torch.full((Hq, T, W), float("-inf"), dtype=torch.float64)
+    cu = case.cu_seqlens_q.long()
+    for b in range(case.batch):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        Lq, L = t1 - t0, int(case.kv_len[b])
+        if Lq == 0 or L == 0:
+            continue
+        nb = -(-L // P)
+        q = case.query[t0:t1].to(torch.float64)              # [Lq, Hq, D]
+        k = request_keys(case, b)                             # [L, Hkv, D]
+        kh = k.repeat_interleave(g, dim=1)                    # [L, Hq, D]
+        s = torch.matmul(q.permute(1, 0, 2), kh.permute(1, 2, 0))   # [Hq, Lq, L]
+        i = torch.arange(Lq)[:, None]
+        j = torch.arange(L)[None, :]
+        qpos = (L - Lq + i) if case.sparse_mode == 3 else torch.full_like(i, L - 1)
+        visible = (j <= qpos) & (j < L)
+        s = s.masked_fill(~visible[None], float("-inf"))
+        pad = torch.full((Hq, Lq, nb * P - L), float("-inf"), dtype=torch.float64)
+        blocks = torch.cat([s, pad], dim=2).reshape(Hq, Lq, nb, P).amax(-1)
+        out[:, t0:t1, :nb] = blocks
+        if case.init_blocks > 0 or case.local_blocks > 0:
+            out[:, t0:t1, :case.init_blocks] = 1e30
+            st = int(case.start_loc[b])
+            lo = max(0, st + 1 - case.local_blocks)
+            if st >= lo:
+                out[:, t0:t1, lo:st + 1] = 1e29
+    return out.to(torch.float32)
