@@ -1,0 +1,189 @@
+"""ctypes binding of libmsa_index_score.so (argument marshalling only).
+
+Every step of the operator runs in the HIP library; this module only turns
+torch tensors into the C ABI's plain descriptors and pointers, passes torch's
+current HIP stream, and turns a non-zero status into an exception.  If the
+library is missing the call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsa_index_score.so")
+
+# msa_dtype_t / msa_layout_t / msa_status_t of include/msa_index_score.h
+DTYPE_CODE = {
+    torch.float16: 0,
+    torch.bfloat16: 1,
+    torch.int8: 2,
+    torch.float8_e4m3fn: 3,
+    torch.float8_e5m2: 4,
+}
+LAYOUT_CODE = {"TND": 0, "BBND": 1, "BNBD": 2}
+STATUS_NAMES = ["MSA_OK", "MSA_ERR_NULL", "MSA_ERR_LAYOUT", "MSA_ERR_DTYPE", "MSA_ERR_SHAPE",
+                "MSA_ERR_STRIDE", "MSA_ERR_SCALE", "MSA_ERR_ATTR", "MSA_ERR_HIP"]
+EXPORTED = ("msa_index_score", "msa_index_score_family", "msa_index_score_out_width",
+            "msa_status_str", "msa_index_score_kernel_family")
+
+
+class MsaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else status}: "
+                         f"{message}")
+        self.status = status
+
+
+class MsaLayoutError(MsaError, ValueError):
+    pass
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load the HIP library (built in-tree by ``block_max_qk_amd.build``)."""
+    global _lib
+    with _lock:
+        if path is None and _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"HIP library {p} is not built; run "
+                               "`python -m block_max_qk_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(p)
+        ptr = ctypes.c_void_p
+        args = [ctypes.POINTER(MsaTensor), ctypes.POINTER(MsaTensor), ptr, ptr, ctypes.c_int64,
+                ptr, ptr, ptr, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                ctypes.c_int32, ptr, ctypes.c_int64, ptr]
+        lib.msa_index_score.argtypes = args
+        lib.msa_index_score.restype = ctypes.c_int
+        lib.msa_index_score_family.argtypes = args + [ctypes.c_int32]
+        lib.msa_index_score_family.restype = ctypes.c_int
+        lib.msa_index_score_out_width.argtypes = [ctypes.c_int64]
+        lib.msa_index_score_out_width.restype = ctypes.c_int64
+        lib.msa_status_str.argtypes = [ctypes.c_int32]
+        lib.msa_status_str.restype = ctypes.c_char_p
+        lib.msa_index_score_kernel_family.argtypes = [ctypes.c_int64, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.c_int32]
+        lib.msa_index_score_kernel_family.restype = ctypes.c_int32
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def describe(t: torch.Tensor, dtype_code: Optional[int] = None) -> MsaTensor:
+    """Descriptor of a tensor: data pointer, element type, shape, strides."""
+    d = MsaTensor()
+    d.data = t.data_ptr() if t.numel() else (t.data_ptr() or None)
+    d.dtype = DTYPE_CODE.get(t.dtype, -1) if dtype_code is None else dtype_code
+    d.ndim = t.dim()
+    for i in range(min(t.dim(), 4)):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _layout_code(layout) -> int:
+    if isinstance(layout, str):
+        return LAYOUT_CODE.get(layout.upper(), -1)
+    return int(layout)
+
+
+def msa_index_score_out_width(max_blocks: int) -> int:
+    return int(load_library().msa_index_score_out_width(int(max_blocks)))
+
+
+def msa_status_str(status: int) -> str:
+    return load_library().msa_status_str(int(status)).decode()
+
+
+def msa_index_score_kernel_family(T: int, batch: int, Hq: int, Hkv: int) -> int:
+    return int(load_library().msa_index_score_kernel_family(int(T), int(batch), int(Hq),
+                                                            int(Hkv)))
+
+
+def msa_index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Tensor,
+                    block_table: Optional[torch.Tensor], scale: Optional[torch.Tensor],
+                    cu_seqlens_q: torch.Tensor, kv_len: torch.Tensor, layout,
+                    sparse_mode: int, init_blocks: int, local_blocks: int, out: torch.Tensor,
+                    max_blocks: int, stream=None, family: int = -1) -> torch.Tensor:
+    """Call the C ABI on device tensors; ``out`` ([Hq, T, W] float32) is filled
+    asynchronously on ``stream`` (default: torch's current stream)."""
+    lib = load_library()
+    dev = out.device
+    for name, t in (("query", query), ("key", key), ("start_loc", start_loc),
+                    ("cu_seqlens_q", cu_seqlens_q), ("kv_len", kv_len),
+                    ("block_table", block_table), ("scale", scale)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, out on {dev}")
+    for name, t in (("start_loc", start_loc), ("cu_seqlens_q", cu_seqlens_q),
+                    ("kv_len", kv_len), ("block_table", block_table)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if scale is not None and (scale.dtype != torch.float32 or not scale.is_contiguous()):
+        raise ValueError("scale must be a contiguous float32 tensor")
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.dim() != 3:
+        raise ValueError("out must be a contiguous float32 [Hq, T, W] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    qd, kd = describe(query), describe(key)
+    args = (ctypes.byref(qd), ctypes.byref(kd), _ptr(start_loc), _ptr(block_table),
+            int(max_blocks), _ptr(scale), _ptr(cu_seqlens_q), _ptr(kv_len),
+            int(kv_len.numel()), _layout_code(layout), int(sparse_mode), int(init_blocks),
+            int(local_blocks), _ptr(out), int(out.shape[2]), ctypes.c_void_p(stream))
+    if family == -1:
+        st = lib.msa_index_score(*args)
+    else:
+        st = lib.msa_index_score_family(*args, int(family))
+    if st != 0:
+        cls = MsaLayoutError if st == 2 else MsaError
+        raise cls(st, msa_status_str(st))
+    return out
+
+
+def index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Tensor, *,
+                block_table: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                actual_seq_qlen: Optional[torch.Tensor] = None,
+                actual_seq_klen: Optional[torch.Tensor] = None, layout_key: str = "BBND",
+                sparse_mode: int = 3, init_blocks: int = 0, local_blocks: int = 1,
+                max_blocks: Optional[int] = None, stream=None, family: int = -1) -> torch.Tensor:
+    """Allocate ``[Hq, T, RoundUp(MB, 16)]`` float32 and fill it.
+
+    ``actual_seq_qlen`` is the ``[B+1]`` query prefix sum, ``actual_seq_klen``
+    the ``[B]`` per-request kv lengths.  MB is ``block_table.shape[1]`` for
+    paged keys; for packed (TND) keys pass ``max_blocks`` or it is read from a
+    host copy of ``actual_seq_klen`` (a device synchronisation).
+    """
+    lay = layout_key.upper() if isinstance(layout_key, str) else layout_key
+    if isinstance(lay, str) and lay not in LAYOUT_CODE:
+        raise ValueError(f"layout_key must be one of TND/BBND/BNBD, got {layout_key!r}")
+    if max_blocks is None:
+        if block_table is not None:
+            max_blocks = int(block_table.shape[1])
+        else:
+            kv = actual_seq_klen.to("cpu", torch.int64)
+            max_blocks = int(((kv + 127) // 128).max()) if kv.numel() else 0
+    W = msa_index_score_out_width(max_blocks)
+    out = torch.empty((query.shape[1], query.shape[0], W), dtype=torch.float32,
+                      device=query.device)
+    return msa_index_score(query, key, start_loc, block_table, scale, actual_seq_qlen,
+                           actual_seq_klen, lay, sparse_mode, init_blocks, local_blocks, out,
+                           max_blocks, stream=stream, family=family)

@@ -1,0 +1,276 @@
+// Device-side building blocks of the MSA index-score kernels (gfx950 only).
+//
+// Terms used below.  A "block" is one logical KV block of P = 128 tokens
+// (one physical page for paged keys).  A "row" is one (query token, index
+// head) pair; the heads of one KV group are the rows that share a key
+// (gitcode cann/ops-transformer issue #4117, section 计算过程: h_kv = h / g).
+// Scores S = K . Q^T are taken on MFMA with the key tokens j as the M side and
+// the rows as the N side, so each lane ends up holding several j of one row in
+// registers and the block maximum is mostly an in-register reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kP = 128;   // tokens per logical block
+constexpr int kD = 128;   // index head dimension
+
+// Element kinds of the key (the query kind follows from it).
+enum KeyKind : int { KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4 };
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// Everything a launch needs; built and validated on the host.
+struct Params {
+  const uint8_t* q;            // query [T, Hq, D]
+  const uint8_t* k;            // key (layout per the strides below)
+  const float* scale;          // int8 dequant scale or nullptr
+  const int32_t* block_table;  // [B, MB] (paged) or nullptr
+  const int32_t* cu_q;         // [B+1]
+  const int32_t* kv_len;       // [B]
+  const int32_t* start_loc;    // [B]
+  float* out;                  // [Hq, T, W]
+  int64_t k_page_stride;       // bytes between physical pages (paged)
+  int32_t k_row_stride;        // bytes between consecutive key tokens
+  int32_t k_head_stride;       // bytes between KV heads
+  int64_t s_page_stride;       // scale elements between pages (paged)
+  int32_t s_row_stride;        // scale elements between tokens
+  int32_t s_head_stride;       // scale elements between KV heads
+  int64_t T;
+  int32_t B, Hq, Hkv, g;
+  int32_t MB, W;
+  int32_t paged, causal;
+  int32_t init_blocks, local_blocks;
+  int32_t hpt;                 // heads of a KV group per tile
+  int32_t tpt;                 // query tokens per tile
+  int32_t hchunks;             // ceil(g / hpt)
+  int32_t chunk;               // blocks per work item
+  int32_t nchunks;             // ceil(W / chunk)
+  int32_t units;               // Hkv * hchunks * nchunks
+  int32_t ntiles;              // upper bound of token tiles over the batch
+};
+
+// ---------------------------------------------------------------------------
+// wave-level helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    T y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ i32x4 ld16(const uint8_t* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Work decomposition.
+//
+// A work item is (unit, tile): a unit is (KV head, head chunk, block chunk),
+// a tile is `tpt` consecutive query tokens of one request.  The hardware
+// hands workgroups to the eight XCDs round-robin by workgroup id, so the id is
+// remapped such that each XCD receives whole units and walks their tiles in
+// order: workgroups that run together on one XCD then read the same key
+// blocks through that XCD's L2, and the units (block ranges of very different
+// cost under the causal window) are dealt across XCDs in turn.
+// ---------------------------------------------------------------------------
+
+struct Work {
+  int valid;
+  int hk, hc, c0, c1;          // KV head, head chunk, block range [c0, c1)
+  int b, t0, ntok;             // request, first token, tokens in the tile
+  int Lq, L;                   // query length and kv_len of the request
+  int64_t koff;                // packed-key offset of the request (TND)
+};
+
+__device__ __forceinline__ Work locate(const Params& p) {
+  Work w;
+  w.valid = 0;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int ui = slot / p.ntiles;
+  const int tile = slot - ui * p.ntiles;
+  const int unit = ui * 8 + xcd;
+  if (unit >= p.units) return w;
+  w.hk = unit / (p.hchunks * p.nchunks);
+  const int rem = unit - w.hk * (p.hchunks * p.nchunks);
+  w.hc = rem / p.nchunks;
+  const int ch = rem - w.hc * p.nchunks;
+  w.c0 = ch * p.chunk;
+  w.c1 = min(w.c0 + p.chunk, p.W);
+
+  // Find the request holding `tile`: a wave-wide prefix sum of the per-request
+  // tile counts ceil(L_q / tpt), 64 requests at a time.
+  const int l = lane_id();
+  int acc = 0;
+  int64_t kacc = 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + l;
+    int lq = 0, kv = 0;
+    if (b < p.B) {
+      lq = p.cu_q[b + 1] - p.cu_q[b];
+      kv = p.kv_len[b];
+    }
+    const int n = (lq + p.tpt - 1) / p.tpt;
+    const int incl = wave_incl_scan(n);
+    const int64_t kincl = wave_incl_scan((int64_t)kv);
+    const int total = __shfl(incl, 63, 64);
+    if (tile < acc + total) {
+      const unsigned long long m = __ballot(acc + incl > tile);
+      const int src = __ffsll((long long)m) - 1;
+      const int n_s = __shfl(n, src, 64);
+      const int incl_s = __shfl(incl, src, 64);
+      const int kv_s = __shfl(kv, src, 64);
+      const int64_t kincl_s = __shfl(kincl, src, 64);
+      w.b = base + src;
+      const int tin = tile - (acc + incl_s - n_s);
+      w.Lq = __shfl(lq, src, 64);
+      w.L = kv_s;
+      w.t0 = p.cu_q[w.b] + tin * p.tpt;
+      w.ntok = min(p.tpt, w.Lq - tin * p.tpt);
+      w.koff = kacc + kincl_s - kv_s;
+      w.valid = 1;
+      return w;
+    }
+    acc += total;
+    kacc += __shfl(kincl, 63, 64);
+  }
+  return w;
+}
+
+// Last visible key index of query token t of the work item's request:
+// min(q_pos, kv_len - 1), with q_pos = kv_len - L_q + i under the right-down
+// causal mode and kv_len - 1 without it (issue #4117, section 计算过程;
+// guide to msa_index_score, section 四: sparse_mode 3 / 0).
+__device__ __forceinline__ int last_visible(const Params& p, const Work& w, int i) {
+  const int qpos = p.causal ? (w.L - w.Lq + i) : (w.L - 1);
+  return min(qpos, w.L - 1);
+}
+
+// Byte offset of key block `beta` of the work item's request (head 0).
+__device__ __forceinline__ int64_t block_offset(const Params& p, const Work& w, int beta) {
+  if (p.paged) {
+    const int64_t page = p.block_table[(int64_t)w.b * p.MB + beta];
+    return page * p.k_page_stride;
+  }
+  return (w.koff + (int64_t)beta * kP) * p.k_row_stride;
+}
+
+// Scale element index of token 0 of block `beta`, head hk.
+__device__ __forceinline__ int64_t scale_offset(const Params& p, const Work& w, int beta,
+                                                int hk) {
+  if (p.paged) {
+    const int64_t page = p.block_table[(int64_t)w.b * p.MB + beta];
+    return page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
+  }
+  return (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
+}
+
+// Final value of output column beta of a row (after the block maximum `v`
+// when the block was scored): -inf fill, then local_mask (guide to
+// msa_index_score, section 二: 1e30 on [0, init_blocks), then 1e29 on
+// [max(0, start_loc+1-local_blocks), start_loc], skipped when both are 0;
+// requests with kv_len = 0 are skipped whole, section 四).
+__device__ __forceinline__ float finish(const Params& p, int L, int start, int beta,
+                                        bool scored, float v) {
+  float r = scored ? v : -__builtin_inff();
+  if (L > 0 && (p.init_blocks > 0 || p.local_blocks > 0)) {
+    if (beta < p.init_blocks) r = 1e30f;
+    const int lo = max(0, start + 1 - p.local_blocks);
+    if (beta >= lo && beta <= start) r = 1e29f;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// element conversion and MFMA wrappers
+// ---------------------------------------------------------------------------
+
+// 4 int8 -> 4 fp16 exactly: bias each byte to u = x + 128, place it in the
+// low mantissa byte of 1024.0h (0x6400 | u = 1024 + u) and subtract 1152.
+__device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) - bias);
+  hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, b) - bias);
+}
+
+// 16 int8 (one i32x4) -> 16 fp16 (two i32x4), byte order kept.
+__device__ __forceinline__ void i8x16_to_f16x16(i32x4 v, i32x4& first, i32x4& second) {
+  uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
+  i8x4_to_f16x4((uint32_t)v.x, a0, a1);
+  i8x4_to_f16x4((uint32_t)v.y, b0, b1);
+  i8x4_to_f16x4((uint32_t)v.z, c0, c1);
+  i8x4_to_f16x4((uint32_t)v.w, d0, d1);
+  first = i32x4{(int)a0, (int)a1, (int)b0, (int)b1};
+  second = i32x4{(int)c0, (int)c1, (int)d0, (int)d1};
+}
+
+// 16x16 output tile, 32-deep k of 16-bit elements.
+template <int KK>
+__device__ __forceinline__ f32x4 mfma16x16x32(i32x4 a, i32x4 b, f32x4 c) {
+  if constexpr (KK == KBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// 32x32 output tile, 16-deep k of 16-bit elements.
+template <int KK>
+__device__ __forceinline__ f32x16 mfma32x32x16(i32x4 a, i32x4 b, f32x16 c) {
+  if constexpr (KK == KBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 cat(i32x4 a, i32x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// OCP fp8 operands: format code 0 = e4m3, 1 = e5m2 (no block scaling).
+template <int KK>
+__device__ __forceinline__ f32x4 mfma16x16x128_f8(i32x8 a, i32x8 b, f32x4 c) {
+  constexpr int fmt = (KK == KF8E5M2) ? 1 : 0;
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, fmt, fmt, 0, 0, 0, 0);
+}
+
+template <int KK>
+__device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c) {
+  constexpr int fmt = (KK == KF8E5M2) ? 1 : 0;
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fmt, fmt, 0, 0, 0, 0);
+}
+
+template <int KK>
+struct Kind {
+  static constexpr bool is_f8 = (KK == KF8E4M3 || KK == KF8E5M2);
+  static constexpr bool is_i8 = (KK == KI8);
+  static constexpr int q_bytes = is_f8 ? 1 : 2;   // query element size
+  static constexpr int k_bytes = (is_f8 || is_i8) ? 1 : 2;
+  static constexpr int mfma_kind = is_i8 ? KF16 : KK;  // operand type fed to MFMA
+};
+
+}  // namespace msa

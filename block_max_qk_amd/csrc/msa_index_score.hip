@@ -1,0 +1,284 @@
+// Host side of the msa_index_score C ABI: argument validation (all of it
+// before any HIP call), work planning, and the launch of one gfx950 kernel on
+// the caller's stream.  The library allocates nothing and keeps no state.
+#include "msa_index_score.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "msa_kernels.hpp"
+
+namespace {
+
+using msa::Params;
+
+int64_t round_up16(int64_t mb) {
+  if (mb < 1) mb = 1;
+  return (mb + 15) / 16 * 16;
+}
+
+int elem_bytes(int32_t dt) {
+  switch (dt) {
+    case MSA_DTYPE_F16:
+    case MSA_DTYPE_BF16: return 2;
+    case MSA_DTYPE_I8:
+    case MSA_DTYPE_F8E4M3:
+    case MSA_DTYPE_F8E5M2: return 1;
+    default: return 0;
+  }
+}
+
+// Supported (query, key) element pairs (guide to msa_index_score, section 七:
+// int8 keys take an fp16 query and a float32 scale; FP8 query and key share
+// one format and take no scale).
+bool pair_ok(int32_t qd, int32_t kd) {
+  if (qd == MSA_DTYPE_F16 && (kd == MSA_DTYPE_F16 || kd == MSA_DTYPE_I8)) return true;
+  if (qd == MSA_DTYPE_BF16 && kd == MSA_DTYPE_BF16) return true;
+  if (qd == MSA_DTYPE_F8E4M3 && kd == MSA_DTYPE_F8E4M3) return true;
+  if (qd == MSA_DTYPE_F8E5M2 && kd == MSA_DTYPE_F8E5M2) return true;
+  return false;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Extent-1 axes are never addressed, so their strides are not compared.
+bool compact_axis(int64_t extent, int64_t stride, int64_t want) {
+  return extent <= 1 || stride == want;
+}
+
+int32_t choose_family(int64_t T, int32_t B, int32_t g) {
+  // Prefill tiles pay off once requests carry about half a 256-row tile of
+  // query rows on average; shorter query runs use 16-row decode tiles.
+  const int64_t rows = T * std::min<int64_t>(g, msa::kPrefillRows);
+  return rows >= (int64_t)(msa::kPrefillRows / 2) * std::max<int32_t>(B, 1) ? 1 : 0;
+}
+
+template <int KK>
+hipError_t launch(int family, const Params& p, int64_t grid, hipStream_t s) {
+  if (family == 1)
+    hipLaunchKernelGGL(msa::prefill_kernel<KK>, dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(msa::decode_kernel<KK>, dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32_t* start_loc,
+                 const int32_t* block_table, int64_t max_blocks, const float* scale,
+                 const int32_t* cu_seqlens_q, const int32_t* kv_len, int32_t batch,
+                 int32_t layout, int32_t sparse_mode, int32_t init_blocks,
+                 int32_t local_blocks, float* out, int64_t out_width, void* stream,
+                 int32_t family) {
+  if (!query || !key || !out || !cu_seqlens_q || !kv_len || !start_loc) return MSA_ERR_NULL;
+  if (layout != MSA_LAYOUT_TND && layout != MSA_LAYOUT_BBND && layout != MSA_LAYOUT_BNBD)
+    return MSA_ERR_LAYOUT;
+  const bool paged = layout != MSA_LAYOUT_TND;
+
+  // element types and scale
+  if (elem_bytes(query->dtype) == 0 || elem_bytes(key->dtype) == 0) return MSA_ERR_DTYPE;
+  if (!pair_ok(query->dtype, key->dtype)) return MSA_ERR_DTYPE;
+  const bool is_i8 = key->dtype == MSA_DTYPE_I8;
+  if (is_i8 != (scale != nullptr)) return MSA_ERR_SCALE;
+
+  // query [T, Hq, D], compact
+  if (query->ndim != 3) return MSA_ERR_SHAPE;
+  const int64_t T = query->shape[0], Hq = query->shape[1], D = query->shape[2];
+  if (T < 0 || Hq < 1 || D != msa::kD) return MSA_ERR_SHAPE;
+  if (!compact_axis(D, query->stride[2], 1) || !compact_axis(Hq, query->stride[1], D) ||
+      !compact_axis(T, query->stride[0], Hq * D))
+    return MSA_ERR_STRIDE;
+
+  // key layout, shape and strides
+  int64_t NP = 0, P = msa::kP, Hkv = 0, KD = 0;
+  int64_t s_page = 0, s_row = 0, s_head = 0;        // element strides
+  const int64_t* ks = key->stride;
+  if (layout == MSA_LAYOUT_TND) {
+    if (key->ndim != 3) return MSA_ERR_SHAPE;
+    NP = key->shape[0];
+    Hkv = key->shape[1];
+    KD = key->shape[2];
+    if (Hkv < 1 || KD != msa::kD || NP < 0) return MSA_ERR_SHAPE;
+    if (!compact_axis(KD, ks[2], 1) || !compact_axis(Hkv, ks[1], KD) ||
+        !compact_axis(NP, ks[0], Hkv * KD))
+      return MSA_ERR_STRIDE;
+    s_row = Hkv * KD;
+    s_head = KD;
+  } else if (layout == MSA_LAYOUT_BBND && key->ndim == 3) {
+    // [NP, P, D]: a single KV head with the head axis left out
+    NP = key->shape[0];
+    P = key->shape[1];
+    Hkv = 1;
+    KD = key->shape[2];
+    if (P != msa::kP || KD != msa::kD || NP < 1) return MSA_ERR_SHAPE;
+    if (!compact_axis(KD, ks[2], 1) || !compact_axis(P, ks[1], KD)) return MSA_ERR_STRIDE;
+    s_page = ks[0];
+    s_row = KD;
+    s_head = 0;
+  } else {
+    if (key->ndim != 4) return MSA_ERR_SHAPE;
+    NP = key->shape[0];
+    KD = key->shape[3];
+    if (layout == MSA_LAYOUT_BBND) {
+      P = key->shape[1];
+      Hkv = key->shape[2];
+    } else {
+      Hkv = key->shape[1];
+      P = key->shape[2];
+    }
+    if (P != msa::kP || KD != msa::kD || Hkv < 1 || NP < 1) return MSA_ERR_SHAPE;
+    if (!compact_axis(KD, ks[3], 1)) return MSA_ERR_STRIDE;
+    if (layout == MSA_LAYOUT_BBND) {
+      if (!compact_axis(Hkv, ks[2], KD) || !compact_axis(P, ks[1], Hkv * KD))
+        return MSA_ERR_STRIDE;
+      s_row = Hkv * KD;
+      s_head = KD;
+    } else {
+      if (!compact_axis(P, ks[2], KD) || !compact_axis(Hkv, ks[1], P * KD))
+        return MSA_ERR_STRIDE;
+      s_row = KD;
+      s_head = P * KD;
+    }
+    s_page = ks[0];
+  }
+  if (Hq % Hkv != 0) return MSA_ERR_SHAPE;
+  if (paged && NP > 1 && s_page < 1) return MSA_ERR_STRIDE;
+  const int kb = elem_bytes(key->dtype);
+  if (paged && ((s_page * kb) % 16) != 0) return MSA_ERR_STRIDE;
+
+  // table, widths and attributes
+  if (max_blocks < 0 || batch < 0) return MSA_ERR_SHAPE;
+  if (paged) {
+    if (!block_table) return MSA_ERR_NULL;
+    if (max_blocks < 1) return MSA_ERR_SHAPE;
+  } else if (block_table) {
+    return MSA_ERR_SHAPE;   // packed keys take no block table
+  }
+  const int64_t W = round_up16(max_blocks);
+  if (out_width != W) return MSA_ERR_SHAPE;
+  if (batch == 0 && T > 0) return MSA_ERR_SHAPE;
+  if (sparse_mode != 0 && sparse_mode != 3) return MSA_ERR_ATTR;
+  const int64_t limit = paged ? max_blocks : W;
+  if (init_blocks < 0 || local_blocks < 0 || init_blocks > limit || local_blocks > limit)
+    return MSA_ERR_ATTR;
+  if (family < -1 || family > 1) return MSA_ERR_ATTR;
+
+  // sizes the kernels index with 32-bit integers
+  if (W > (1 << 24) || Hq > (1 << 16) || batch > (1 << 30) || T > (int64_t(1) << 31) - 1 ||
+      s_row * kb > INT32_MAX || s_head * kb > INT32_MAX)
+    return MSA_ERR_SHAPE;
+
+  if (!aligned16(query->data) || !aligned16(key->data) || !aligned16(out))
+    return MSA_ERR_STRIDE;
+
+  if (T == 0) return MSA_OK;
+
+  // plan
+  const int32_t g = (int32_t)(Hq / Hkv);
+  const int fam = family >= 0 ? family : choose_family(T, batch, g);
+  const int rows = fam == 1 ? msa::kPrefillRows : msa::kDecodeRows;
+  Params p{};
+  p.q = static_cast<const uint8_t*>(query->data);
+  p.k = static_cast<const uint8_t*>(key->data);
+  p.scale = scale;
+  p.block_table = paged ? block_table : nullptr;
+  p.cu_q = cu_seqlens_q;
+  p.kv_len = kv_len;
+  p.start_loc = start_loc;
+  p.out = out;
+  p.k_page_stride = paged ? s_page * kb : 0;
+  p.k_row_stride = (int32_t)(s_row * kb);
+  p.k_head_stride = Hkv > 1 ? (int32_t)(s_head * kb) : 0;
+  if (paged) {
+    p.s_page_stride = Hkv * msa::kP;   // scale [NP, Hkv, P]
+    p.s_head_stride = msa::kP;
+    p.s_row_stride = 1;
+  } else {
+    p.s_page_stride = 0;               // scale [T2, Hkv]
+    p.s_head_stride = 1;
+    p.s_row_stride = (int32_t)Hkv;
+  }
+  p.T = T;
+  p.B = batch;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.g = g;
+  p.MB = (int32_t)std::max<int64_t>(max_blocks, 1);
+  p.W = (int32_t)W;
+  p.paged = paged ? 1 : 0;
+  p.causal = sparse_mode == 3 ? 1 : 0;
+  p.init_blocks = init_blocks;
+  p.local_blocks = local_blocks;
+  p.hpt = std::min<int32_t>(g, rows);
+  p.tpt = rows / p.hpt;
+  p.hchunks = (g + p.hpt - 1) / p.hpt;
+  p.chunk = fam == 1 ? msa::kPrefillChunk : 16;
+  p.nchunks = (int32_t)((W + p.chunk - 1) / p.chunk);
+  p.units = p.Hkv * p.hchunks * p.nchunks;
+  const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
+  p.ntiles = (int32_t)std::min<int64_t>(T, bound);
+  const int64_t units8 = ((int64_t)p.units + 7) / 8 * 8;
+  const int64_t grid = units8 * p.ntiles;
+  if (grid > INT32_MAX || (int64_t)p.units * p.ntiles > INT32_MAX) return MSA_ERR_SHAPE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (key->dtype) {
+    case MSA_DTYPE_F16: e = launch<msa::KF16>(fam, p, grid, s); break;
+    case MSA_DTYPE_BF16: e = launch<msa::KBF16>(fam, p, grid, s); break;
+    case MSA_DTYPE_I8: e = launch<msa::KI8>(fam, p, grid, s); break;
+    case MSA_DTYPE_F8E4M3: e = launch<msa::KF8E4M3>(fam, p, grid, s); break;
+    default: e = launch<msa::KF8E5M2>(fam, p, grid, s); break;
+  }
+  return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
+                             const int32_t* start_loc, const int32_t* block_table,
+                             int64_t max_blocks, const float* scale,
+                             const int32_t* cu_seqlens_q, const int32_t* kv_len,
+                             int32_t batch, int32_t layout, int32_t sparse_mode,
+                             int32_t init_blocks, int32_t local_blocks, float* out,
+                             int64_t out_width, void* stream) {
+  return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
+             layout, sparse_mode, init_blocks, local_blocks, out, out_width, stream, -1);
+}
+
+msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_t* key,
+                                    const int32_t* start_loc, const int32_t* block_table,
+                                    int64_t max_blocks, const float* scale,
+                                    const int32_t* cu_seqlens_q, const int32_t* kv_len,
+                                    int32_t batch, int32_t layout, int32_t sparse_mode,
+                                    int32_t init_blocks, int32_t local_blocks, float* out,
+                                    int64_t out_width, void* stream, int32_t family) {
+  return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
+             layout, sparse_mode, init_blocks, local_blocks, out, out_width, stream, family);
+}
+
+int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }
+
+int32_t msa_index_score_kernel_family(int64_t T, int32_t batch, int32_t Hq, int32_t Hkv) {
+  if (Hkv < 1) Hkv = 1;
+  return choose_family(T, batch, std::max<int32_t>(Hq / Hkv, 1));
+}
+
+const char* msa_status_str(int32_t s) {
+  switch (s) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_NULL: return "a required pointer is NULL";
+    case MSA_ERR_LAYOUT: return "layout must be TND, BBND or BNBD";
+    case MSA_ERR_DTYPE: return "unsupported query/key element types";
+    case MSA_ERR_SHAPE: return "inconsistent shapes";
+    case MSA_ERR_STRIDE: return "non-compact or misaligned axis";
+    case MSA_ERR_SCALE: return "scale must be given exactly for int8 keys";
+    case MSA_ERR_ATTR: return "sparse_mode, init_blocks, local_blocks or family out of range";
+    case MSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

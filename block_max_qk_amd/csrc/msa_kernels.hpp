@@ -1,0 +1,369 @@
+// MSA index-score kernels for gfx950.
+//
+// Both kernels compute, for one work item (KV head, head chunk, range of
+// blocks, tile of query tokens of one request), the block maximum
+//   score[h, t, beta] = max_{visible j in beta} < q[t, h], k~[j, h / g] >
+// (gitcode cann/ops-transformer issue #4117, section 计算过程; the order
+// DOT -> DEQUANT -> MASK -> MAX) and write the tile's rows of columns
+// [c0, c1) of the [Hq, T, W] float32 output, including the -inf fill and the
+// local_mask constants.
+//
+// decode_kernel  -- 16 rows per tile (the g heads of a KV group for one or a
+//   few tokens).  Key traffic dominates and nothing is reused across rows, so
+//   each of the four waves streams whole blocks straight from HBM into MFMA
+//   operand registers (16x16 tiles, key tokens on M, rows on N) and many
+//   waves per CU keep enough bytes in flight.
+// prefill_kernel -- 256 rows per tile (32 tokens x 8 heads for g = 8).  A key
+//   block is loaded once per workgroup with coalesced 16-byte loads, written
+//   to LDS in a bank-conflict-free XOR-swizzled layout (int8 is converted to
+//   fp16 on the way), and read by all four waves, each holding 64 query rows
+//   in registers (32x32 MFMA tiles, key tokens on M).
+//
+// In both, a lane's accumulators hold several key tokens of one row, so the
+// 128-wide block maximum is an in-register max over the lane's values (after
+// the int8 column scale and, on blocks cut by the causal window or kv_len, a
+// select to -inf) followed by one or two cross-lane steps.
+#pragma once
+
+#include "msa_device.hpp"
+
+namespace msa {
+
+constexpr int kDecodeRows = 16;
+constexpr int kDecodeChunkMax = 64;
+constexpr int kPrefillRows = 256;
+constexpr int kPrefillChunk = 16;
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+
+template <int KK>
+__global__ __launch_bounds__(256) void decode_kernel(Params p) {
+  using Kd = Kind<KK>;
+  __shared__ float res[kDecodeRows][kDecodeChunkMax + 1];
+
+  const Work w = locate(p);
+  if (!w.valid) return;
+
+  const int wave = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
+  const int G = l >> 4;          // this lane's k group, 0..3
+  const int i0 = w.t0 - p.cu_q[w.b];
+
+  // the row this lane reads and reduces
+  const int ti = n / p.hpt;
+  const int hl = n - ti * p.hpt;
+  const int hg = w.hc * p.hpt + hl;               // head index inside the KV group
+  const bool row_ok = (n < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
+  const int lim = row_ok ? last_visible(p, w, i0 + ti) : -1;
+
+  const int nb = min((w.L + kP - 1) / kP, p.MB);
+  const int lim_lo = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0) : -1;
+  const int lim_hi = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0 + w.ntok - 1) : -1;
+  const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
+
+  // query operand (N side), zero for rows outside the tile
+  i32x4 qv[4];
+  if constexpr (Kd::is_f8) {
+    qv[0] = qv[1] = i32x4{0, 0, 0, 0};
+    if (row_ok) {
+      const uint8_t* qr = p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD;
+      qv[0] = ld16(qr + 32 * G);
+      qv[1] = ld16(qr + 32 * G + 16);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[s] = i32x4{0, 0, 0, 0};
+    if (row_ok) {
+      const uint8_t* qr = p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD * 2;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // 16-bit keys: k step s holds 8-element chunk 4s+G of the row;
+        // int8 keys:   chunk 4G+s (a lane's 32 key bytes are contiguous).
+        const int c = Kd::is_i8 ? (4 * G + s) : (4 * s + G);
+        qv[s] = ld16(qr + 16 * c);
+      }
+    }
+  }
+
+  for (int beta = w.c0 + wave; beta < vend; beta += 4) {
+    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
+    const int nvalid = min(kP, w.L - beta * kP);
+    const bool full = beta * kP + kP - 1 <= lim_lo;
+    const float* sb = nullptr;
+    if constexpr (Kd::is_i8) sb = p.scale + scale_offset(p, w, beta, w.hk);
+
+    float m = -__builtin_inff();
+    if constexpr (Kd::is_f8 || Kd::is_i8) {
+      // one byte per element: a lane reads 32 contiguous bytes of its token
+      i32x4 kv[8][2];
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+        const int jj = jt * 16 + n;
+        if (jj < nvalid) {
+          const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride + 32 * G;
+          kv[jt][0] = ld16(kr);
+          kv[jt][1] = ld16(kr + 16);
+        } else {
+          kv[jt][0] = kv[jt][1] = i32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (Kd::is_f8) {
+          acc = mfma16x16x128_f8<KK>(cat(kv[jt][0], kv[jt][1]), cat(qv[0], qv[1]), acc);
+        } else {
+          i32x4 a0, a1, a2, a3;
+          i8x16_to_f16x16(kv[jt][0], a0, a1);
+          i8x16_to_f16x16(kv[jt][1], a2, a3);
+          acc = mfma16x16x32<KF16>(a0, qv[0], acc);
+          acc = mfma16x16x32<KF16>(a1, qv[1], acc);
+          acc = mfma16x16x32<KF16>(a2, qv[2], acc);
+          acc = mfma16x16x32<KF16>(a3, qv[3], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jr = jt * 16 + 4 * G + r;         // key token of acc[r]
+          float v = acc[r];
+          if constexpr (Kd::is_i8) v *= (jr < nvalid) ? sb[(int64_t)jr * p.s_row_stride] : 0.f;
+          if (!full) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
+          m = fmaxf(m, v);
+        }
+      }
+    } else {
+      i32x4 kv[8][4];
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+        const int jj = jt * 16 + n;
+        if (jj < nvalid) {
+          const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) kv[jt][s] = ld16(kr + 16 * (4 * s + G));
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) kv[jt][s] = i32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma16x16x32<KK>(kv[jt][s], qv[s], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jr = jt * 16 + 4 * G + r;
+          float v = acc[r];
+          if (!full) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
+          m = fmaxf(m, v);
+        }
+      }
+    }
+    // the four k groups hold disjoint key tokens of the same row
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (G == 0) res[n][beta - w.c0] = m;
+  }
+  __syncthreads();
+
+  const int cols = w.c1 - w.c0;
+  const int start = p.start_loc[w.b];
+  for (int e = threadIdx.x; e < kDecodeRows * p.chunk; e += 256) {
+    const int r = e / p.chunk;
+    const int col = e - r * p.chunk;
+    if (col >= cols) continue;
+    const int ri = r / p.hpt;
+    const int rh = w.hc * p.hpt + (r - ri * p.hpt);
+    if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
+    const int beta = w.c0 + col;
+    const int64_t h = (int64_t)w.hk * p.g + rh;
+    const int64_t t = w.t0 + ri;
+    p.out[(h * p.T + t) * p.W + beta] = finish(p, w.L, start, beta, beta < vend, res[r][col]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill
+// ---------------------------------------------------------------------------
+
+template <int KK>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
+  using Kd = Kind<KK>;
+  // bytes per key token in LDS: fp8 stays fp8, int8 is widened to fp16
+  constexpr int RB = Kd::is_f8 ? 128 : 256;
+  constexpr int PASSES = Kd::is_f8 || Kd::is_i8 ? 4 : 8;   // 16-byte global loads per thread
+  __shared__ __attribute__((aligned(16))) uint8_t kl[kP * RB];
+  __shared__ float scl[kP];
+  __shared__ float res[kPrefillRows][kPrefillChunk + 1];
+
+  const Work w = locate(p);
+  if (!w.valid) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int l = lane_id();
+  const int n = l & 31;          // row within an N tile / key token within an M tile
+  const int G = l >> 5;          // k group, 0..1
+  const int i0 = w.t0 - p.cu_q[w.b];
+
+  int lim[2];
+  i32x4 qv[2][8];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = wave * 64 + nt * 32 + n;
+    const int ti = r / p.hpt;
+    const int hg = w.hc * p.hpt + (r - ti * p.hpt);
+    const bool ok = (r < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
+    lim[nt] = ok ? last_visible(p, w, i0 + ti) : -1;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[nt][s] = i32x4{0, 0, 0, 0};
+    if (ok) {
+      const uint8_t* qr =
+          p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD * Kd::q_bytes;
+      if constexpr (Kd::is_f8) {
+        // k step s (64 deep) of group G: bytes [64s + 32G, +32)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          qv[nt][2 * s] = ld16(qr + 64 * s + 32 * G);
+          qv[nt][2 * s + 1] = ld16(qr + 64 * s + 32 * G + 16);
+        }
+      } else {
+        // k step s (16 deep) of group G: 8-element chunk 2s+G
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qv[nt][s] = ld16(qr + 16 * (2 * s + G));
+      }
+    }
+  }
+
+  const int nb = min((w.L + kP - 1) / kP, p.MB);
+  const int lim_lo = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0) : -1;
+  const int lim_hi = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0 + w.ntok - 1) : -1;
+  const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
+
+  // staging: thread -> (token, 16-byte chunk) of the key block
+  constexpr int CPR = Kd::k_bytes == 2 ? 16 : 8;      // global 16-byte chunks per token
+  constexpr int TPP = 256 / CPR;                       // tokens per pass
+  const int sc = tid % CPR;
+  const int sj = tid / CPR;
+  i32x4 st[PASSES];
+  float sv = 0.f;
+
+  auto gload = [&](int beta) {
+    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
+    const int nvalid = min(kP, w.L - beta * kP);
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int jj = ps * TPP + sj;
+      st[ps] = (jj < nvalid) ? ld16(kb + (int64_t)jj * p.k_row_stride + 16 * sc)
+                             : i32x4{0, 0, 0, 0};
+    }
+    if constexpr (Kd::is_i8) {
+      if (tid < kP)
+        sv = (tid < nvalid)
+                 ? p.scale[scale_offset(p, w, beta, w.hk) + (int64_t)tid * p.s_row_stride]
+                 : 0.f;
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int jj = ps * TPP + sj;
+      if constexpr (Kd::is_f8) {
+        *reinterpret_cast<i32x4*>(kl + jj * 128 + ((sc ^ ((jj >> 1) & 7)) << 4)) = st[ps];
+      } else if constexpr (Kd::is_i8) {
+        i32x4 a, b;
+        i8x16_to_f16x16(st[ps], a, b);
+        *reinterpret_cast<i32x4*>(kl + jj * 256 + (((2 * sc) ^ (jj & 15)) << 4)) = a;
+        *reinterpret_cast<i32x4*>(kl + jj * 256 + (((2 * sc + 1) ^ (jj & 15)) << 4)) = b;
+      } else {
+        *reinterpret_cast<i32x4*>(kl + jj * 256 + ((sc ^ (jj & 15)) << 4)) = st[ps];
+      }
+    }
+    if constexpr (Kd::is_i8) {
+      if (tid < kP) scl[tid] = sv;
+    }
+  };
+
+  if (w.c0 < vend) gload(w.c0);
+  for (int beta = w.c0; beta < vend; ++beta) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (beta + 1 < vend) gload(beta + 1);
+
+    const bool full = beta * kP + kP - 1 <= lim_lo;
+    float run0 = -__builtin_inff(), run1 = -__builtin_inff();
+#pragma unroll 1
+    for (int mt = 0; mt < 4; ++mt) {
+      const int jj = mt * 32 + n;
+      f32x16 acc0 = {}, acc1 = {};
+      if constexpr (Kd::is_f8) {
+        const int sw = (jj >> 1) & 7;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int c = 4 * s + 2 * G;
+          const i32x4 a0 = *reinterpret_cast<const i32x4*>(kl + jj * 128 + ((c ^ sw) << 4));
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(kl + jj * 128 + (((c + 1) ^ sw) << 4));
+          const i32x8 a = cat(a0, a1);
+          acc0 = mfma32x32x64_f8<KK>(a, cat(qv[0][2 * s], qv[0][2 * s + 1]), acc0);
+          acc1 = mfma32x32x64_f8<KK>(a, cat(qv[1][2 * s], qv[1][2 * s + 1]), acc1);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int c = 2 * s + G;
+          const i32x4 a = *reinterpret_cast<const i32x4*>(kl + jj * 256 + ((c ^ (jj & 15)) << 4));
+          acc0 = mfma32x32x16<Kd::mfma_kind>(a, qv[0][s], acc0);
+          acc1 = mfma32x32x16<Kd::mfma_kind>(a, qv[1][s], acc1);
+        }
+      }
+      // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+        float v0 = acc0[r], v1 = acc1[r];
+        if constexpr (Kd::is_i8) {
+          const float s = scl[jr];
+          v0 *= s;
+          v1 *= s;
+        }
+        if (!full) {
+          const int j = beta * kP + jr;
+          v0 = (j <= lim[0]) ? v0 : -__builtin_inff();
+          v1 = (j <= lim[1]) ? v1 : -__builtin_inff();
+        }
+        run0 = fmaxf(run0, v0);
+        run1 = fmaxf(run1, v1);
+      }
+    }
+    // the two k groups hold the two halves of each 32-token M tile
+    run0 = fmaxf(run0, __shfl_xor(run0, 32, 64));
+    run1 = fmaxf(run1, __shfl_xor(run1, 32, 64));
+    res[wave * 64 + G * 32 + n][beta - w.c0] = G ? run1 : run0;
+  }
+  __syncthreads();
+
+  // one thread per row writes the row's columns [c0, c1)
+  const int r = tid;
+  const int ti = r / p.hpt;
+  const int hg = w.hc * p.hpt + (r - ti * p.hpt);
+  if (r < p.hpt * p.tpt && ti < w.ntok && hg < p.g) {
+    const int start = p.start_loc[w.b];
+    const int64_t h = (int64_t)w.hk * p.g + hg;
+    float* o = p.out + (h * p.T + (w.t0 + ti)) * p.W + w.c0;
+    const int cols = w.c1 - w.c0;   // a multiple of 4: W and c0 are multiples of 16
+    for (int c = 0; c < cols; c += 4) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int beta = w.c0 + c + e;
+        v[e] = finish(p, w.L, start, beta, beta < vend, res[r][c + e]);
+      }
+      *reinterpret_cast<f32x4*>(o + c) = v;
+    }
+  }
+}
+
+}  // namespace msa

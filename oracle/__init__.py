@@ -43,6 +43,15 @@ _lock = threading.Lock()
 _lib = None
 
 
+def default_threads() -> int:
+    """Worker threads when the caller passes 0: OMP_NUM_THREADS if set, else
+    up to 16 of the host's cores."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def build(force: bool = False, out: str = LIB, src: str = SRC) -> str:
     """Compile the oracle (gcc, -O2, no FP contraction)."""
     if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
@@ -152,7 +161,7 @@ def index_score(query, key, layout, start_loc, block_table, scale, cu_seqlens_q,
                                   init_blocks, local_blocks)
     W = out_width(max_blocks, lib)
     out = torch.empty((Hq, T, W), dtype=torch.float32)
-    rc = lib.orc_index_score(*args, out.data_ptr(), int(nthreads))
+    rc = lib.orc_index_score(*args, out.data_ptr(), int(nthreads or default_threads()))
     if rc < 0:
         raise ValueError(f"oracle: inputs break the caller contract (code {rc})")
     del keep
@@ -170,7 +179,7 @@ def index_score_points(query, key, layout, start_loc, block_table, scale, cu_seq
     pts = points.to(torch.int64).contiguous()
     vals = torch.empty(pts.shape[0], dtype=torch.float32)
     rc = lib.orc_index_score_points(*args, pts.data_ptr(), pts.shape[0], vals.data_ptr(),
-                                    int(nthreads))
+                                    int(nthreads or default_threads()))
     if rc < 0:
         raise ValueError(f"oracle: inputs break the caller contract (code {rc})")
     del keep

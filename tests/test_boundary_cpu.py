@@ -1,0 +1,202 @@
+"""The C ABI on the CPU: the library loads, exports every declared function, and
+rejects each malformed call with its status before touching the GPU.
+
+No call here reaches a kernel launch: every one fails validation or has T = 0
+(which returns without launching).
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+import torch
+
+import block_max_qk_amd as m
+from block_max_qk_amd._binding import MsaTensor, describe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa_index_score.h")
+
+OK, NULL, LAYOUT, DTYPE, SHAPE, STRIDE, SCALE, ATTR = range(8)
+DT = {"f16": 0, "bf16": 1, "i8": 2, "e4m3": 3, "e5m2": 4}
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(m.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == set(m.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_out_width_matches_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "out_width.json")))
+    for mb, w in g["max_blocks_to_width"]:
+        assert m.msa_index_score_out_width(mb) == w
+
+
+def test_status_strings():
+    for s in range(9):
+        assert m.msa_status_str(s)
+    assert m.msa_status_str(99) == "unknown status"
+
+
+def test_kernel_family_choice():
+    assert m.msa_index_score_kernel_family(64, 64, 16, 1) == 0        # decode batch
+    assert m.msa_index_score_kernel_family(32, 32, 16, 1) == 0        # int8 decode batch
+    assert m.msa_index_score_kernel_family(15360, 4, 32, 4) == 1      # varlen prefill
+    assert m.msa_index_score_kernel_family(4096, 1, 64, 8) == 1       # chunked prefill
+    assert m.msa_index_score_kernel_family(32, 1, 8, 1) == 1          # tiny prefill
+
+
+# ---------------------------------------------------------------------------
+# validation: fake device addresses, never dereferenced
+# ---------------------------------------------------------------------------
+
+FAKE = 0x7F0000000000
+
+
+def tdesc(shape, stride=None, dtype=0, addr=FAKE):
+    d = MsaTensor()
+    d.data = addr
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    for i, (a, b) in enumerate(zip(shape, stride)):
+        d.shape[i] = a
+        d.stride[i] = b
+    return d
+
+
+def call(q=None, k=None, *, start=FAKE, table=FAKE, mb=2, scale=None, cu=FAKE, kv=FAKE, B=1,
+         layout=1, mode=3, init=0, local=1, out=FAKE, width=16, family=None):
+    lib = m.load_library()
+    q = q if q is not None else tdesc([32, 8, 128], dtype=DT["f16"])
+    k = k if k is not None else tdesc([8, 128, 1, 128], dtype=DT["f16"])
+    args = [ctypes.byref(q) if q is not False else None,
+            ctypes.byref(k) if k is not False else None,
+            start, table, mb, scale, cu, kv, B, layout, mode, init, local, out, width, None]
+    if family is None:
+        return lib.msa_index_score(*args)
+    return lib.msa_index_score_family(*args, family)
+
+
+def test_valid_empty_call_returns_ok_without_launch():
+    q = tdesc([0, 8, 128], dtype=DT["f16"])
+    assert call(q=q, B=1) == OK
+
+
+def test_null_pointers():
+    assert call(q=False) == NULL
+    assert call(k=False) == NULL
+    assert call(out=None) == NULL
+    assert call(cu=None) == NULL
+    assert call(kv=None) == NULL
+    assert call(start=None) == NULL
+    assert call(table=None) == NULL              # paged layouts need a block table
+
+
+@pytest.mark.parametrize("layout", [-1, 3, 7])
+def test_bad_layout(layout):
+    assert call(layout=layout) == LAYOUT
+
+
+def test_python_layout_key_is_case_insensitive_and_checked():
+    with pytest.raises(ValueError):
+        m.index_score(torch.zeros(1, 8, 128, dtype=torch.float16),
+                      torch.zeros(2, 128, 1, 128, dtype=torch.float16),
+                      torch.zeros(1, dtype=torch.int32), layout_key="bhsd",
+                      block_table=torch.zeros(1, 2, dtype=torch.int32),
+                      actual_seq_qlen=torch.tensor([0, 1], dtype=torch.int32),
+                      actual_seq_klen=torch.tensor([1], dtype=torch.int32))
+
+
+@pytest.mark.parametrize("qd,kd,with_scale,want", [
+    ("bf16", "f16", False, DTYPE),      # mixed 16-bit types
+    ("f16", "bf16", False, DTYPE),
+    ("bf16", "i8", True, DTYPE),        # int8 keys need an fp16 query
+    ("e4m3", "e5m2", False, DTYPE),     # FP8 query and key of one format
+    ("e4m3", "f16", False, DTYPE),
+    ("f16", "i8", False, SCALE),        # int8 without scale
+    ("f16", "f16", True, SCALE),        # scale with a non-int8 key
+    ("e4m3", "e4m3", True, SCALE),
+])
+def test_dtype_and_scale_rules(qd, kd, with_scale, want):
+    q = tdesc([4, 8, 128], dtype=DT[qd])
+    k = tdesc([8, 128, 1, 128], dtype=DT[kd])
+    assert call(q=q, k=k, scale=FAKE if with_scale else None) == want
+
+
+def test_unknown_dtype_code():
+    assert call(q=tdesc([4, 8, 128], dtype=9)) == DTYPE
+
+
+def test_shape_rules():
+    assert call(q=tdesc([4, 8, 64], dtype=0)) == SHAPE                           # D != 128
+    assert call(k=tdesc([8, 64, 1, 128], dtype=0)) == SHAPE                      # P != 128
+    assert call(k=tdesc([8, 128, 3, 128], dtype=0)) == SHAPE                     # Hq % Hkv
+    assert call(k=tdesc([8, 1, 128, 128], dtype=0), layout=1) == SHAPE           # BNBD shape as BBND
+    assert call(k=tdesc([128, 1, 128], dtype=0), layout=1) == SHAPE              # 3-D TND shape as BBND
+    assert call(width=32) == SHAPE                                               # out width
+    assert call(mb=0) == SHAPE                                                   # paged MB >= 1
+    assert call(B=0) == SHAPE                                                    # T > 0, no requests
+    assert call(layout=0, k=tdesc([300, 1, 128], dtype=0), table=FAKE) == SHAPE  # TND takes no table
+
+
+def test_three_dim_bbnd_and_tnd_accepted_shapes_with_t0():
+    q0 = tdesc([0, 8, 128], dtype=0)
+    assert call(q=q0, k=tdesc([8, 128, 128], dtype=0), layout=1) == OK
+    assert call(q=q0, k=tdesc([300, 1, 128], dtype=0), layout=0, table=None, mb=3) == OK
+    assert call(q=q0, k=tdesc([0, 1, 128], dtype=0), layout=0, table=None, mb=0) == OK
+
+
+def test_stride_rules():
+    # dim0 gap is allowed for paged keys
+    gap = tdesc([8, 128, 1, 128], [3 * 128 * 128, 128, 128, 1], dtype=0)
+    assert call(q=tdesc([0, 8, 128], dtype=0), k=gap) == OK
+    # inner axes must be compact
+    bad = tdesc([8, 128, 2, 128], [128 * 2 * 128, 2 * 128, 256, 1], dtype=0)
+    assert call(k=bad, q=tdesc([4, 8, 128], dtype=0)) == STRIDE
+    bad_d = tdesc([8, 128, 1, 128], [128 * 128 * 2, 256, 128, 2], dtype=0)
+    assert call(k=bad_d) == STRIDE
+    # an extent-1 head axis is not addressed: any stride is fine
+    odd = tdesc([8, 128, 1, 128], [128 * 128, 128, 7, 1], dtype=0)
+    assert call(q=tdesc([0, 8, 128], dtype=0), k=odd) == OK
+    # TND keys must be fully compact
+    tnd = tdesc([300, 2, 128], [512, 128, 1], dtype=0)
+    assert call(q=tdesc([4, 8, 128], dtype=0), k=tnd, layout=0, table=None, mb=3) == STRIDE
+    # query must be compact
+    assert call(q=tdesc([4, 8, 128], [2048, 128, 1], dtype=0)) == STRIDE
+    # misaligned pointers / page strides
+    assert call(q=tdesc([4, 8, 128], dtype=0, addr=FAKE + 2)) == STRIDE
+    mis = tdesc([8, 128, 1, 128], [128 * 128 + 1, 128, 128, 1], dtype=0)
+    assert call(k=mis) == STRIDE
+    assert call(out=FAKE + 4) == STRIDE
+
+
+def test_attribute_rules():
+    assert call(mode=1) == ATTR
+    assert call(mode=2) == ATTR
+    assert call(init=-1) == ATTR
+    assert call(local=-1) == ATTR
+    assert call(init=3, mb=2) == ATTR                 # paged limit: MB
+    assert call(local=3, mb=2) == ATTR
+    q0 = tdesc([0, 8, 128], dtype=0)
+    assert call(q=q0, init=2, local=2, mb=2) == OK
+    # packed keys: limit is the aligned output width
+    tnd = tdesc([300, 1, 128], dtype=0)
+    assert call(q=q0, k=tnd, layout=0, table=None, mb=3, init=16, local=16) == OK
+    assert call(q=q0, k=tnd, layout=0, table=None, mb=3, init=17) == ATTR
+    assert call(family=2) == ATTR
+    assert call(family=-2) == ATTR
