@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of msa_index_score on one MI355X.
+
+A step is one call of the operator (one kernel launch through the C ABI) over
+one batch of seeded synthetic inputs resident in HBM.  The default workload is
+the decode batch: 64 requests of one query token, 16 index heads over one KV
+head, kv_len ~ U[1, 32768], bf16 keys in 16384 paged 128-token blocks
+(BBND) behind a random block table, right-down causal, local_blocks = 1.
+
+Timed region: W untimed warmup steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); every launch is also bracketed by HIP events on the
+launch stream, which give the kernel's average duration for the roofline.
+To keep the 256 MB Infinity Cache from serving repeated reads, the key cache
+is replicated into several HBM copies and the steps rotate over them.
+
+Output: one JSON line (rank 0 of 1).  ``--config all`` prints one line per
+workload instead (for measurement; the default line is the headline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("block scores/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill), 1 GPU")
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 2500.0, "f8e4m3": 5000.0, "f8e5m2": 5000.0}
+ESIZE = {"f16": 2, "bf16": 2, "i8": 1, "f8e4m3": 1, "f8e5m2": 1}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_max_qk_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def workload_stats(case) -> dict:
+    """Algorithmic work of one step, from the drawn lengths."""
+    import torch
+    P = case.block_size
+    cu = case.cu_seqlens_q.long()
+    kv = case.kv_len.long()
+    B = case.batch
+    scores = 0          # (h, t, beta) entries with >= 1 visible key
+    visible = 0         # (h, t, j) visible key positions
+    k_bytes = 0
+    table_bytes = 0
+    esz = ESIZE[case.key_dtype_name()]
+    for b in range(B):
+        Lq = int(cu[b + 1] - cu[b])
+        L = int(kv[b])
+        if Lq == 0 or L == 0:
+            continue
+        i = torch.arange(Lq, dtype=torch.int64)
+        qpos = (L - Lq + i) if case.sparse_mode == 3 else torch.full_like(i, L - 1)
+        lim = torch.clamp(torch.minimum(qpos, torch.tensor(L - 1)), min=-1)
+        lim = torch.minimum(lim, torch.tensor(case.max_blocks * P - 1))
+        nvis = torch.where(lim >= 0, lim // P + 1, torch.zeros_like(lim))
+        scores += int(nvis.sum()) * case.Hq
+        visible += int((lim + 1).sum()) * case.Hq
+        lmax = int(lim.max())
+        if lmax >= 0:
+            k_bytes += (lmax + 1) * case.Hkv * case.D * esz      # each visible key read once
+            if case.scale is not None:
+                k_bytes += (lmax + 1) * case.Hkv * 4
+            if case.layout != "TND":
+                table_bytes += (lmax // P + 1) * 4
+    W = ((max(case.max_blocks, 1) + 15) // 16) * 16
+    q_bytes = case.query.numel() * case.query.element_size()
+    out_bytes = case.Hq * case.T * W * 4
+    return {"scores": scores, "out_entries": case.Hq * case.T * W,
+            "flops": 2 * case.D * visible,
+            "bytes": k_bytes + q_bytes + out_bytes + table_bytes + 8 * B,
+            "k_bytes": k_bytes, "q_bytes": q_bytes, "out_bytes": out_bytes}
+
+
+def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
+                 cpu_baseline: bool, args) -> dict:
+    import torch
+    import block_max_qk_amd as m
+    from block_max_qk_amd._binding import describe
+    import ctypes
+    import synth
+
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    case = synth.config_case(c_idx)
+    t_gen = time.time() - t_gen
+    stats = workload_stats(case)
+    kname = case.key_dtype_name()
+    is_decode = m.msa_index_score_kernel_family(case.T, case.batch, case.Hq, case.Hkv) == 0 \
+        if family < 0 else family == 0
+
+    # inputs resident in HBM; the key cache (and scale) replicated `copies` times
+    W = m.msa_index_score_out_width(case.max_blocks)
+    q = case.query.to(dev)
+    keys, scales = [], []
+    for _ in range(copies):
+        ks = case.key_storage.to(dev)
+        keys.append(ks[:: case.gap + 1] if case.gap else ks)
+        scales.append(None if case.scale is None else case.scale.to(dev))
+    sl = case.start_loc.to(dev)
+    bt = None if case.block_table is None else case.block_table.to(dev)
+    cu = case.cu_seqlens_q.to(dev)
+    kv = case.kv_len.to(dev)
+    out = torch.empty((case.Hq, case.T, W), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = m.load_library()
+
+    # marshal each copy's arguments once; the timed loop only calls the C ABI
+    keep = []
+    calls = []
+    for i in range(copies):
+        qd, kd = describe(q), describe(keys[i])
+        keep += [qd, kd]
+        a = (ctypes.byref(qd), ctypes.byref(kd), ctypes.c_void_p(sl.data_ptr()),
+             None if bt is None else ctypes.c_void_p(bt.data_ptr()), case.max_blocks,
+             None if scales[i] is None else ctypes.c_void_p(scales[i].data_ptr()),
+             ctypes.c_void_p(cu.data_ptr()), ctypes.c_void_p(kv.data_ptr()), case.batch,
+             m._binding.LAYOUT_CODE[case.layout], case.sparse_mode, case.init_blocks,
+             case.local_blocks, ctypes.c_void_p(out.data_ptr()), W,
+             ctypes.c_void_p(stream.cuda_stream), family)
+        calls.append(a)
+    fn = lib.msa_index_score_family
+
+    def step(i):
+        st = fn(*calls[i % copies])
+        if st != 0:
+            raise RuntimeError(m.msa_status_str(st))
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev0[i].record(stream)
+        step(i)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
+    kernel_ms = sum(kms) / len(kms)
+    ms_per_step = (t1 - t0) * 1e3 / steps
+
+    gbs = stats["bytes"] / (kernel_ms * 1e-3) / 1e9
+    tflops = stats["flops"] / (kernel_ms * 1e-3) / 1e12
+    if is_decode:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        pk = PEAK_TFLOPS[kname]
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": pk, "unit": "TFLOP/s",
+                "frac": round(tflops / pk, 4)}
+    roof["traffic"] = measured_traffic(case.name)
+    roof["kernel"] = ("decode_kernel" if is_decode else "prefill_kernel") + f"<{kname}>"
+    roof["kernel_ms_avg"] = round(kernel_ms, 5)
+    roof["kernel_ms_median"] = round(kms[len(kms) // 2], 5)
+    roof["algorithmic_bytes"] = stats["bytes"]
+    roof["algorithmic_flops"] = stats["flops"]
+
+    value = stats["scores"] / (ms_per_step * 1e-3)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "block scores/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": kname, "data": "synthetic",
+        "config": {"workload": case.name, "B": case.batch, "T": case.T, "Hq": case.Hq,
+                   "Hkv": case.Hkv, "D": case.D, "P": case.block_size, "MB": case.max_blocks,
+                   "layout": case.layout, "query_dtype": case.query_dtype_name(),
+                   "key_dtype": kname, "sparse_mode": case.sparse_mode,
+                   "init_blocks": case.init_blocks, "local_blocks": case.local_blocks,
+                   "key_cache_copies": copies, "kernel_family": "decode" if is_decode
+                   else "prefill"},
+        "hbm_gbs": round(gbs, 1), "mfma_tflops": round(tflops, 3),
+        "block_scores_per_step": stats["scores"], "out_entries_per_step": stats["out_entries"],
+        "roofline": roof,
+        "cpu_baseline": None,
+        "input_generation_s": round(t_gen, 2),
+    }
+    del calls, keep
+    if cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_leg(case, stats, args)
+    return res
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, when
+    they were taken on the current kernel sources; otherwise null."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline_leg(case, stats, args) -> dict:
+    """The CPU oracle, as it is, timed on this host on a bounded sample of the
+    same workload, scaled to block scores/s."""
+    import torch
+    import oracle
+    nth = oracle.default_threads()
+    if case.T <= 256:
+        t0 = time.perf_counter()
+        oracle.index_score(**oracle.case_args(case), nthreads=nth)
+        dt = time.perf_counter() - t0
+        return {"value": round(stats["scores"] / dt, 1), "unit": "block scores/s", "cores": nth,
+                "kind": "oracle", "sample": f"the whole workload ({stats['scores']} block "
+                f"scores) in {dt:.2f} s"}
+    # prefill: whole rows (h, t, all blocks) of tokens spread over the batch
+    g = torch.Generator().manual_seed(7)
+    nrows = args.cpu_rows
+    ts = torch.randint(0, case.T, (nrows,), generator=g)
+    hs = torch.randint(0, case.Hq, (nrows,), generator=g)
+    W = ((max(case.max_blocks, 1) + 15) // 16) * 16
+    beta = torch.arange(W)
+    pts = torch.stack([hs.repeat_interleave(W), ts.repeat_interleave(W), beta.repeat(nrows)], 1)
+    t0 = time.perf_counter()
+    vals = oracle.index_score_case_points(case, pts, nthreads=nth)
+    dt = time.perf_counter() - t0
+    # block scores of the sampled rows: the finite, non-forced entries
+    sampled = int((torch.isfinite(vals) & (vals.abs() < 1e28)).sum())
+    return {"value": round(sampled / dt, 1), "unit": "block scores/s", "cores": nth,
+            "kind": "oracle", "sample": f"{nrows} whole rows (h, t) at random, {sampled} "
+            f"block scores in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_bbnd_bf16",
+                    help="workload name, index 0-4, or 'all'")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="key-cache copies to rotate over (0: enough to exceed 1 GiB)")
+    ap.add_argument("--family", type=int, default=-1, help="-1 auto, 0 decode, 1 prefill tiles")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="instead of the operator, run this many MiB device copies "
+                         "(counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the operator has no cross-GPU step here "
+              "(see the sharding notes in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": max(args.steps, 1)}))
+        return
+
+    import synth
+    names = list(synth.CONFIG_NAMES)
+    if args.config == "all":
+        todo = list(range(len(names)))
+    elif args.config.isdigit():
+        todo = [int(args.config)]
+    else:
+        todo = [names.index(args.config)]
+    for c in todo:
+        copies = args.copies
+        if copies <= 0:
+            copies = 4 if c in (1, 3) else 1
+        r = bench_config(c, args.steps, args.warmup, copies, args.family,
+                         not args.no_cpu_baseline, args)
+        print(json.dumps(r), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,7 +70,11 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
                  int32_t layout, int32_t sparse_mode, int32_t init_blocks,
                  int32_t local_blocks, float* out, int64_t out_width, void* stream,
                  int32_t family) {
-  if (!query || !key || !out || !cu_seqlens_q || !kv_len || !start_loc) return MSA_ERR_NULL;
+  // Pointers that a call with no requests (B = 0) or no query tokens (T = 0)
+  // never reads may be NULL there; torch hands empty tensors a NULL address.
+  if (!query || !key || !cu_seqlens_q) return MSA_ERR_NULL;
+  if (batch > 0 && (!kv_len || !start_loc)) return MSA_ERR_NULL;
+  if (query->ndim == 3 && query->shape[0] > 0 && !out) return MSA_ERR_NULL;
   if (layout != MSA_LAYOUT_TND && layout != MSA_LAYOUT_BBND && layout != MSA_LAYOUT_BNBD)
     return MSA_ERR_LAYOUT;
   const bool paged = layout != MSA_LAYOUT_TND;
@@ -149,7 +153,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   // table, widths and attributes
   if (max_blocks < 0 || batch < 0) return MSA_ERR_SHAPE;
   if (paged) {
-    if (!block_table) return MSA_ERR_NULL;
+    if (!block_table && batch > 0) return MSA_ERR_NULL;
     if (max_blocks < 1) return MSA_ERR_SHAPE;
   } else if (block_table) {
     return MSA_ERR_SHAPE;   // packed keys take no block table

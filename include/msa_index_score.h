@@ -114,6 +114,9 @@ typedef struct {
  * sum(kv_len) = T2 and ceil(kv_len[b]/128) <= MB.  Blocks at or past MB are
  * never scored or read, whatever kv_len says.
  *
+ * NULL is accepted for pointers the call cannot read: kv_len, start_loc and
+ * block_table when batch = 0, and out when T = 0.
+ *
  * Ownership: every pointer is caller-owned; the library allocates no device
  * memory and keeps no state between calls.  Returns MSA_OK or an error
  * status; T = 0 returns MSA_OK without launching anything.  query, key and

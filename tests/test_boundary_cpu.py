@@ -95,6 +95,9 @@ def call(q=None, k=None, *, start=FAKE, table=FAKE, mb=2, scale=None, cu=FAKE, k
 def test_valid_empty_call_returns_ok_without_launch():
     q = tdesc([0, 8, 128], dtype=DT["f16"])
     assert call(q=q, B=1) == OK
+    assert call(q=q, B=1, out=None) == OK                      # T = 0: out never written
+    assert call(q=q, B=0, kv=None, start=None, table=None) == OK   # no requests
+    assert call(q=q, B=1, kv=None) == NULL
 
 
 def test_null_pointers():
