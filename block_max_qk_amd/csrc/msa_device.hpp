@@ -79,6 +79,14 @@ __device__ __forceinline__ i32x4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }
 
+// Streaming load for data read once per launch (decode key blocks): the
+// nontemporal hint keeps single-use lines from displacing reused ones in the
+// caches, which on MI355X more than doubles the rate of random 32 KB block
+// reads compared with plain loads.
+__device__ __forceinline__ i32x4 ld16_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Work decomposition.
 //

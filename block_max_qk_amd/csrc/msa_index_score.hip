@@ -56,11 +56,22 @@ int32_t choose_family(int64_t T, int32_t B, int32_t g) {
 }
 
 template <int KK>
-hipError_t launch(int family, const Params& p, int64_t grid, hipStream_t s) {
-  if (family == 1)
-    hipLaunchKernelGGL(msa::prefill_kernel<KK>, dim3((unsigned)grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(msa::decode_kernel<KK>, dim3((unsigned)grid), dim3(256), 0, s, p);
+hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
+  if (family == 1) {
+    hipLaunchKernelGGL(msa::prefill_kernel<KK>, dim3((unsigned)prefill_grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  // Decode: one round of workgroups, as many as fit on the device at once,
+  // split evenly over the units (KV head x head chunk).
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK>, 256, 0);
+  if (e != hipSuccess) return e;
+  const int64_t slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+  const int64_t gu = std::max<int64_t>(1, slots / p.units);
+  hipLaunchKernelGGL(msa::decode_kernel<KK>, dim3((unsigned)(gu * p.units)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -216,8 +227,10 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hpt = std::min<int32_t>(g, rows);
   p.tpt = rows / p.hpt;
   p.hchunks = (g + p.hpt - 1) / p.hpt;
-  p.chunk = fam == 1 ? msa::kPrefillChunk : 16;
-  p.nchunks = (int32_t)((W + p.chunk - 1) / p.chunk);
+  // prefill units: (KV head, head chunk, block chunk); decode units: (KV
+  // head, head chunk), each walking its own copy of the batch's work list
+  p.chunk = msa::kPrefillChunk;
+  p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
   p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
   p.ntiles = (int32_t)std::min<int64_t>(T, bound);

@@ -30,70 +30,241 @@
 namespace msa {
 
 constexpr int kDecodeRows = 16;
-constexpr int kDecodeChunkMax = 64;
 constexpr int kPrefillRows = 256;
 constexpr int kPrefillChunk = 16;
 
 // ---------------------------------------------------------------------------
 // decode
+//
+// The batch's work is the list of (tile, visible block) pairs, tiles in
+// request order and blocks ascending; its length N is known only on the
+// device.  Each workgroup takes an equal contiguous slice of the list and its
+// four waves take every fourth pair of the slice, so every wave streams about
+// the same number of key blocks whatever the spread of kv_len.  The grid is
+// one round of workgroups (as many as the chip holds at once), so no
+// workgroup waits for a slot.  Columns a tile cannot see (past its last
+// visible block, up to the output width) are written by a fill pass.
 // ---------------------------------------------------------------------------
+
+// Visible blocks of tile j of a request (kv_len L, L_q query tokens): up to
+// the block of the tile's last visible key, never past MB.
+__device__ __forceinline__ int tile_blocks(const Params& p, int L, int Lq, int j) {
+  if (L <= 0) return 0;
+  const int ilast = min((j + 1) * p.tpt, Lq) - 1;
+  const int qpos = p.causal ? (L - Lq + ilast) : (L - 1);
+  const int lim = min(qpos, L - 1);
+  return lim < 0 ? 0 : min(lim / kP + 1, p.MB);
+}
+
+__device__ __forceinline__ int tiles_of(const Params& p, int Lq) {
+  return (Lq + p.tpt - 1) / p.tpt;
+}
+
+// Position in the work list.
+struct Cursor {
+  int b, j, beta, nvis;    // request, tile of the request, block, blocks of the tile
+  int cu, Lq, L;           // cu_seqlens_q[b], L_q, kv_len
+  int64_t koff;            // packed-key offset of the request
+};
+
+// Totals over the batch: work-list length and number of tiles.
+__device__ __forceinline__ void count_work(const Params& p, int& ntask, int& ntile) {
+  const int l = lane_id();
+  int acc = 0, acct = 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + l;
+    int tasks = 0, tiles = 0;
+    if (b < p.B) {
+      const int lq = p.cu_q[b + 1] - p.cu_q[b];
+      const int kv = p.kv_len[b];
+      tiles = tiles_of(p, lq);
+      for (int j = 0; j < tiles; ++j) tasks += tile_blocks(p, kv, lq, j);
+    }
+    acc += __shfl(wave_incl_scan(tasks), 63, 64);
+    acct += __shfl(wave_incl_scan(tiles), 63, 64);
+  }
+  ntask = acc;
+  ntile = acct;
+}
+
+// Cursor at work-list entry tau (< N).  With by_tile, tau counts tiles
+// instead and the cursor lands on block 0 of tile tau.
+__device__ __forceinline__ void seek(const Params& p, int tau, bool by_tile, Cursor& c) {
+  const int l = lane_id();
+  int acc = 0;
+  int64_t kacc = 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + l;
+    int lq = 0, kv = 0, cnt = 0;
+    if (b < p.B) {
+      lq = p.cu_q[b + 1] - p.cu_q[b];
+      kv = p.kv_len[b];
+      const int tiles = tiles_of(p, lq);
+      if (by_tile) {
+        cnt = tiles;
+      } else {
+        for (int j = 0; j < tiles; ++j) cnt += tile_blocks(p, kv, lq, j);
+      }
+    }
+    const int incl = wave_incl_scan(cnt);
+    const int64_t kincl = wave_incl_scan((int64_t)kv);
+    const int total = __shfl(incl, 63, 64);
+    if (tau < acc + total) {
+      const int src = __ffsll((long long)__ballot(acc + incl > tau)) - 1;
+      c.b = base + src;
+      c.Lq = __shfl(lq, src, 64);
+      c.L = __shfl(kv, src, 64);
+      c.koff = kacc + __shfl(kincl, src, 64) - c.L;
+      c.cu = p.cu_q[c.b];
+      int local = tau - (acc + __shfl(incl, src, 64) - __shfl(cnt, src, 64));
+      if (by_tile) {
+        c.j = local;
+        c.beta = 0;
+        c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
+        return;
+      }
+      for (int j = 0;; ++j) {
+        const int nv = tile_blocks(p, c.L, c.Lq, j);
+        if (local < nv) {
+          c.j = j;
+          c.beta = local;
+          c.nvis = nv;
+          return;
+        }
+        local -= nv;
+      }
+    }
+    acc += total;
+    kacc += __shfl(kincl, 63, 64);
+  }
+}
+
+// Move the cursor `step` entries forward; the caller guarantees the target
+// entry exists.
+__device__ __forceinline__ void advance(const Params& p, Cursor& c, int step) {
+  c.beta += step;
+  while (c.beta >= c.nvis) {
+    c.beta -= c.nvis;
+    ++c.j;
+    while (c.j >= tiles_of(p, c.Lq)) {
+      c.koff += c.L;
+      ++c.b;
+      c.cu = p.cu_q[c.b];
+      c.Lq = p.cu_q[c.b + 1] - c.cu;
+      c.L = p.kv_len[c.b];
+      c.j = 0;
+    }
+    c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
+  }
+}
+
+// Work of the cursor's tile as seen by the block helpers.
+__device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int hk, int hc) {
+  Work w;
+  w.valid = 1;
+  w.hk = hk;
+  w.hc = hc;
+  w.c0 = 0;
+  w.c1 = p.W;
+  w.b = c.b;
+  w.t0 = c.cu + c.j * p.tpt;
+  w.ntok = min(p.tpt, c.Lq - c.j * p.tpt);
+  w.Lq = c.Lq;
+  w.L = c.L;
+  w.koff = c.koff;
+  return w;
+}
 
 template <int KK>
 __global__ __launch_bounds__(256) void decode_kernel(Params p) {
   using Kd = Kind<KK>;
-  __shared__ float res[kDecodeRows][kDecodeChunkMax + 1];
-
-  const Work w = locate(p);
-  if (!w.valid) return;
-
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
   const int G = l >> 4;          // this lane's k group, 0..3
-  const int i0 = w.t0 - p.cu_q[w.b];
 
-  // the row this lane reads and reduces
-  const int ti = n / p.hpt;
-  const int hl = n - ti * p.hpt;
-  const int hg = w.hc * p.hpt + hl;               // head index inside the KV group
-  const bool row_ok = (n < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
-  const int lim = row_ok ? last_visible(p, w, i0 + ti) : -1;
+  const int unit = blockIdx.x % p.units;
+  const int wi = blockIdx.x / p.units;
+  const int gu = gridDim.x / p.units;
+  const int hk = unit / p.hchunks;
+  const int hc = unit - hk * p.hchunks;
 
-  const int nb = min((w.L + kP - 1) / kP, p.MB);
-  const int lim_lo = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0) : -1;
-  const int lim_hi = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0 + w.ntok - 1) : -1;
-  const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
+  int ntask, ntile;
+  count_work(p, ntask, ntile);
 
-  // query operand (N side), zero for rows outside the tile
-  i32x4 qv[4];
-  if constexpr (Kd::is_f8) {
-    qv[0] = qv[1] = i32x4{0, 0, 0, 0};
-    if (row_ok) {
-      const uint8_t* qr = p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD;
-      qv[0] = ld16(qr + 32 * G);
-      qv[1] = ld16(qr + 32 * G + 16);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qv[s] = i32x4{0, 0, 0, 0};
-    if (row_ok) {
-      const uint8_t* qr = p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD * 2;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        // 16-bit keys: k step s holds 8-element chunk 4s+G of the row;
-        // int8 keys:   chunk 4G+s (a lane's 32 key bytes are contiguous).
-        const int c = Kd::is_i8 ? (4 * G + s) : (4 * s + G);
-        qv[s] = ld16(qr + 16 * c);
-      }
+  // fill pass: tiles wi, wi + gu, ... get -inf (and local_mask) on the
+  // columns past their last visible block
+  for (int k = wi; k < ntile; k += gu) {
+    Cursor c;
+    seek(p, k, true, c);
+    const Work w = tile_work(p, c, hk, hc);
+    const int start = p.start_loc[w.b];
+    const int ncol = p.W - c.nvis;
+    for (int e = threadIdx.x; e < kDecodeRows * ncol; e += 256) {
+      const int r = e / ncol;
+      const int beta = c.nvis + (e - r * ncol);
+      const int ri = r / p.hpt;
+      const int rh = hc * p.hpt + (r - ri * p.hpt);
+      if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
+      const int64_t h = (int64_t)hk * p.g + rh;
+      p.out[(h * p.T + (w.t0 + ri)) * p.W + beta] = finish(p, w.L, start, beta, false, 0.f);
     }
   }
 
-  for (int beta = w.c0 + wave; beta < vend; beta += 4) {
-    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
+  // compute pass over this workgroup's slice of the work list
+  const int per = (ntask + gu - 1) / gu;
+  const int s0 = wi * per;
+  const int s1 = min(ntask, s0 + per);
+  int task = s0 + wave;
+  if (task >= s1) return;
+
+  Cursor c;
+  seek(p, task, false, c);
+  int cur_b = -1, cur_j = -1;
+  Work w;
+  i32x4 qv[4];
+  int lim = -1, lim_lo = -1, start = 0;
+  bool row_ok = false;
+  int ti = 0, hg = 0;
+  for (;;) {
+    if (c.b != cur_b || c.j != cur_j) {
+      // new tile: its query rows, windows and local_mask anchor
+      cur_b = c.b;
+      cur_j = c.j;
+      w = tile_work(p, c, hk, hc);
+      const int i0 = c.j * p.tpt;
+      ti = n / p.hpt;
+      hg = hc * p.hpt + (n - ti * p.hpt);
+      row_ok = (n < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
+      lim = row_ok ? last_visible(p, w, i0 + ti) : -1;
+      lim_lo = last_visible(p, w, i0);
+      start = p.start_loc[w.b];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qv[s] = i32x4{0, 0, 0, 0};
+      if (row_ok) {
+        const uint8_t* qr =
+            p.q + ((int64_t)(w.t0 + ti) * p.Hq + (hk * p.g + hg)) * kD * Kd::q_bytes;
+        if constexpr (Kd::is_f8) {
+          qv[0] = ld16(qr + 32 * G);
+          qv[1] = ld16(qr + 32 * G + 16);
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            // 16-bit keys: k step s holds 8-element chunk 4s+G of the row;
+            // int8 keys:   chunk 4G+s (a lane's 32 key bytes are contiguous).
+            const int ch = Kd::is_i8 ? (4 * G + s) : (4 * s + G);
+            qv[s] = ld16(qr + 16 * ch);
+          }
+        }
+      }
+    }
+
+    const int beta = c.beta;
+    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
     const bool full = beta * kP + kP - 1 <= lim_lo;
     const float* sb = nullptr;
-    if constexpr (Kd::is_i8) sb = p.scale + scale_offset(p, w, beta, w.hk);
+    if constexpr (Kd::is_i8) sb = p.scale + scale_offset(p, w, beta, hk);
 
     float m = -__builtin_inff();
     if constexpr (Kd::is_f8 || Kd::is_i8) {
@@ -104,8 +275,8 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
         const int jj = jt * 16 + n;
         if (jj < nvalid) {
           const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride + 32 * G;
-          kv[jt][0] = ld16(kr);
-          kv[jt][1] = ld16(kr + 16);
+          kv[jt][0] = ld16_stream(kr);
+          kv[jt][1] = ld16_stream(kr + 16);
         } else {
           kv[jt][0] = kv[jt][1] = i32x4{0, 0, 0, 0};
         }
@@ -128,7 +299,9 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
         for (int r = 0; r < 4; ++r) {
           const int jr = jt * 16 + 4 * G + r;         // key token of acc[r]
           float v = acc[r];
-          if constexpr (Kd::is_i8) v *= (jr < nvalid) ? sb[(int64_t)jr * p.s_row_stride] : 0.f;
+          if constexpr (Kd::is_i8)
+            v *= (jr < nvalid) ? __builtin_nontemporal_load(sb + (int64_t)jr * p.s_row_stride)
+                               : 0.f;
           if (!full) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
           m = fmaxf(m, v);
         }
@@ -141,7 +314,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
         if (jj < nvalid) {
           const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) kv[jt][s] = ld16(kr + 16 * (4 * s + G));
+          for (int s = 0; s < 4; ++s) kv[jt][s] = ld16_stream(kr + 16 * (4 * s + G));
         } else {
 #pragma unroll
           for (int s = 0; s < 4; ++s) kv[jt][s] = i32x4{0, 0, 0, 0};
@@ -164,23 +337,14 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
     // the four k groups hold disjoint key tokens of the same row
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (G == 0) res[n][beta - w.c0] = m;
-  }
-  __syncthreads();
+    if (G == 0 && row_ok) {
+      const int64_t h = (int64_t)hk * p.g + hg;
+      p.out[(h * p.T + (w.t0 + ti)) * p.W + beta] = finish(p, w.L, start, beta, true, m);
+    }
 
-  const int cols = w.c1 - w.c0;
-  const int start = p.start_loc[w.b];
-  for (int e = threadIdx.x; e < kDecodeRows * p.chunk; e += 256) {
-    const int r = e / p.chunk;
-    const int col = e - r * p.chunk;
-    if (col >= cols) continue;
-    const int ri = r / p.hpt;
-    const int rh = w.hc * p.hpt + (r - ri * p.hpt);
-    if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
-    const int beta = w.c0 + col;
-    const int64_t h = (int64_t)w.hk * p.g + rh;
-    const int64_t t = w.t0 + ri;
-    p.out[(h * p.T + t) * p.W + beta] = finish(p, w.L, start, beta, beta < vend, res[r][col]);
+    task += 4;
+    if (task >= s1) break;
+    advance(p, c, 4);
   }
 }
 
