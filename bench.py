@@ -153,6 +153,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     t1 = time.perf_counter()
     kms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
     kernel_ms = sum(kms) / len(kms)
+    span_ms = ev0[0].elapsed_time(ev1[steps - 1]) / steps
     ms_per_step = (t1 - t0) * 1e3 / steps
 
     gbs = stats["bytes"] / (kernel_ms * 1e-3) / 1e9
@@ -167,6 +168,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     roof["traffic"] = measured_traffic(case.name)
     roof["kernel"] = ("decode_kernel" if is_decode else "prefill_kernel") + f"<{kname}>"
     roof["kernel_ms_avg"] = round(kernel_ms, 5)
+    roof["gpu_ms_per_step_span"] = round(span_ms, 5)
     roof["kernel_ms_median"] = round(kms[len(kms) // 2], 5)
     roof["algorithmic_bytes"] = stats["bytes"]
     roof["algorithmic_flops"] = stats["flops"]

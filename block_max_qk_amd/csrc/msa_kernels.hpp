@@ -67,54 +67,60 @@ struct Cursor {
   int64_t koff;            // packed-key offset of the request
 };
 
-// Totals over the batch: work-list length and number of tiles.
-__device__ __forceinline__ void count_work(const Params& p, int& ntask, int& ntile) {
-  const int l = lane_id();
-  int acc = 0, acct = 0;
-  for (int base = 0; base < p.B; base += 64) {
-    const int b = base + l;
-    int tasks = 0, tiles = 0;
-    if (b < p.B) {
-      const int lq = p.cu_q[b + 1] - p.cu_q[b];
-      const int kv = p.kv_len[b];
-      tiles = tiles_of(p, lq);
-      for (int j = 0; j < tiles; ++j) tasks += tile_blocks(p, kv, lq, j);
-    }
-    acc += __shfl(wave_incl_scan(tasks), 63, 64);
-    acct += __shfl(wave_incl_scan(tiles), 63, 64);
+// Per-lane view of 64 consecutive requests: lengths, their work-list and
+// tile counts, and wave-wide inclusive prefix sums of those.
+struct Scan64 {
+  int lq, kv, tasks, tiles;
+  int inc_tasks, inc_tiles;
+  int64_t inc_kv;
+};
+
+__device__ __forceinline__ Scan64 scan64(const Params& p, int base) {
+  Scan64 s;
+  const int b = base + lane_id();
+  s.lq = s.kv = s.tasks = s.tiles = 0;
+  if (b < p.B) {
+    s.lq = p.cu_q[b + 1] - p.cu_q[b];
+    s.kv = p.kv_len[b];
+    s.tiles = tiles_of(p, s.lq);
+    for (int j = 0; j < s.tiles; ++j) s.tasks += tile_blocks(p, s.kv, s.lq, j);
   }
-  ntask = acc;
-  ntile = acct;
+  s.inc_tasks = wave_incl_scan(s.tasks);
+  s.inc_tiles = wave_incl_scan(s.tiles);
+  s.inc_kv = wave_incl_scan((int64_t)s.kv);
+  return s;
+}
+
+// Totals over the batch: work-list length and number of tiles.  A batch of
+// at most 64 requests is scanned once and `first` is kept for seek().
+__device__ __forceinline__ void count_work(const Params& p, Scan64& first, int& ntask,
+                                           int& ntile) {
+  ntask = ntile = 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const Scan64 s = scan64(p, base);
+    if (base == 0) first = s;
+    ntask += __shfl(s.inc_tasks, 63, 64);
+    ntile += __shfl(s.inc_tiles, 63, 64);
+  }
 }
 
 // Cursor at work-list entry tau (< N).  With by_tile, tau counts tiles
 // instead and the cursor lands on block 0 of tile tau.
-__device__ __forceinline__ void seek(const Params& p, int tau, bool by_tile, Cursor& c) {
-  const int l = lane_id();
+__device__ __forceinline__ void seek(const Params& p, const Scan64& first, int tau,
+                                     bool by_tile, Cursor& c) {
   int acc = 0;
   int64_t kacc = 0;
   for (int base = 0; base < p.B; base += 64) {
-    const int b = base + l;
-    int lq = 0, kv = 0, cnt = 0;
-    if (b < p.B) {
-      lq = p.cu_q[b + 1] - p.cu_q[b];
-      kv = p.kv_len[b];
-      const int tiles = tiles_of(p, lq);
-      if (by_tile) {
-        cnt = tiles;
-      } else {
-        for (int j = 0; j < tiles; ++j) cnt += tile_blocks(p, kv, lq, j);
-      }
-    }
-    const int incl = wave_incl_scan(cnt);
-    const int64_t kincl = wave_incl_scan((int64_t)kv);
+    const Scan64 s = base == 0 ? first : scan64(p, base);
+    const int cnt = by_tile ? s.tiles : s.tasks;
+    const int incl = by_tile ? s.inc_tiles : s.inc_tasks;
     const int total = __shfl(incl, 63, 64);
     if (tau < acc + total) {
       const int src = __ffsll((long long)__ballot(acc + incl > tau)) - 1;
       c.b = base + src;
-      c.Lq = __shfl(lq, src, 64);
-      c.L = __shfl(kv, src, 64);
-      c.koff = kacc + __shfl(kincl, src, 64) - c.L;
+      c.Lq = __shfl(s.lq, src, 64);
+      c.L = __shfl(s.kv, src, 64);
+      c.koff = kacc + __shfl(s.inc_kv, src, 64) - c.L;
       c.cu = p.cu_q[c.b];
       int local = tau - (acc + __shfl(incl, src, 64) - __shfl(cnt, src, 64));
       if (by_tile) {
@@ -135,7 +141,7 @@ __device__ __forceinline__ void seek(const Params& p, int tau, bool by_tile, Cur
       }
     }
     acc += total;
-    kacc += __shfl(kincl, 63, 64);
+    kacc += __shfl(s.inc_kv, 63, 64);
   }
 }
 
@@ -176,7 +182,7 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
 }
 
 template <int KK>
-__global__ __launch_bounds__(256) void decode_kernel(Params p) {
+__global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
   using Kd = Kind<KK>;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
@@ -190,13 +196,14 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
   const int hc = unit - hk * p.hchunks;
 
   int ntask, ntile;
-  count_work(p, ntask, ntile);
+  Scan64 first;
+  count_work(p, first, ntask, ntile);
 
   // fill pass: tiles wi, wi + gu, ... get -inf (and local_mask) on the
   // columns past their last visible block
   for (int k = wi; k < ntile; k += gu) {
     Cursor c;
-    seek(p, k, true, c);
+    seek(p, first, k, true, c);
     const Work w = tile_work(p, c, hk, hc);
     const int start = p.start_loc[w.b];
     const int ncol = p.W - c.nvis;
@@ -219,11 +226,11 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
   if (task >= s1) return;
 
   Cursor c;
-  seek(p, task, false, c);
+  seek(p, first, task, false, c);
   int cur_b = -1, cur_j = -1;
   Work w;
   i32x4 qv[4];
-  int lim = -1, lim_lo = -1, start = 0;
+  int lim = -1, lim_lo = -1, start = 0, next_page = -1;
   bool row_ok = false;
   int ti = 0, hg = 0;
   for (;;) {
@@ -260,7 +267,16 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
     }
 
     const int beta = c.beta;
-    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)hk * p.k_head_stride;
+    int64_t boff;
+    if (p.paged) {
+      // the page was fetched during the previous block when it was known
+      if (next_page < 0) next_page = p.block_table[(int64_t)w.b * p.MB + beta];
+      boff = (int64_t)next_page * p.k_page_stride;
+    } else {
+      boff = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
+    }
+    next_page = -1;
+    const uint8_t* kb = p.k + boff + (int64_t)hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
     const bool full = beta * kP + kP - 1 <= lim_lo;
     const float* sb = nullptr;
@@ -281,6 +297,9 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
           kv[jt][0] = kv[jt][1] = i32x4{0, 0, 0, 0};
         }
       }
+      // next block's page index, if it belongs to the same tile
+      if (p.paged && beta + 4 < c.nvis && task + 4 < s1)
+        next_page = p.block_table[(int64_t)w.b * p.MB + beta + 4];
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -295,13 +314,22 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
           acc = mfma16x16x32<KF16>(a2, qv[2], acc);
           acc = mfma16x16x32<KF16>(a3, qv[3], acc);
         }
+        f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (Kd::is_i8) {
+          const int jr0 = jt * 16 + 4 * G;
+          if (p.s_row_stride == 1 && jr0 + 3 < nvalid) {
+            sc4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sb + jr0));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sc4[r] = (jr0 + r < nvalid) ? sb[(int64_t)(jr0 + r) * p.s_row_stride] : 0.f;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int jr = jt * 16 + 4 * G + r;         // key token of acc[r]
           float v = acc[r];
-          if constexpr (Kd::is_i8)
-            v *= (jr < nvalid) ? __builtin_nontemporal_load(sb + (int64_t)jr * p.s_row_stride)
-                               : 0.f;
+          if constexpr (Kd::is_i8) v *= sc4[r];
           if (!full) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
           m = fmaxf(m, v);
         }
@@ -320,6 +348,9 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p) {
           for (int s = 0; s < 4; ++s) kv[jt][s] = i32x4{0, 0, 0, 0};
         }
       }
+      // next block's page index, if it belongs to the same tile
+      if (p.paged && beta + 4 < c.nvis && task + 4 < s1)
+        next_page = p.block_table[(int64_t)w.b * p.MB + beta + 4];
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
