@@ -25,6 +25,8 @@
 // select to -inf) followed by one or two cross-lane steps.
 #pragma once
 
+#include <type_traits>
+
 #include "msa_device.hpp"
 
 namespace msa {
@@ -388,10 +390,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
   using Kd = Kind<KK>;
   // bytes per key token in LDS: fp8 stays fp8, int8 is widened to fp16
   constexpr int RB = Kd::is_f8 ? 128 : 256;
-  constexpr int PASSES = Kd::is_f8 || Kd::is_i8 ? 4 : 8;   // 16-byte global loads per thread
-  __shared__ __attribute__((aligned(16))) uint8_t kl[kP * RB];
-  __shared__ float scl[kP];
-  __shared__ float res[kPrefillRows][kPrefillChunk + 1];
+  constexpr int BUF = kP * RB;                 // one key block in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t kl[2 * BUF];
+  __shared__ float scl[2][kP];
 
   const Work w = locate(p);
   if (!w.valid) return;
@@ -402,6 +403,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
   const int n = l & 31;          // row within an N tile / key token within an M tile
   const int G = l >> 5;          // k group, 0..1
   const int i0 = w.t0 - p.cu_q[w.b];
+
+  const int nb = min((w.L + kP - 1) / kP, p.MB);
+  const int lim_lo = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0) : -1;
+  const int lim_hi = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0 + w.ntok - 1) : -1;
+  const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
+  const bool busy = w.c0 < vend;      // some block of this work item is visible
 
   int lim[2];
   i32x4 qv[2][8];
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
     lim[nt] = ok ? last_visible(p, w, i0 + ti) : -1;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qv[nt][s] = i32x4{0, 0, 0, 0};
-    if (ok) {
+    if (ok && busy) {
       const uint8_t* qr =
           p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD * Kd::q_bytes;
       if constexpr (Kd::is_f8) {
@@ -432,116 +439,164 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
     }
   }
 
-  const int nb = min((w.L + kP - 1) / kP, p.MB);
-  const int lim_lo = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0) : -1;
-  const int lim_hi = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0 + w.ntok - 1) : -1;
-  const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
-
-  // staging: thread -> (token, 16-byte chunk) of the key block
-  constexpr int CPR = Kd::k_bytes == 2 ? 16 : 8;      // global 16-byte chunks per token
-  constexpr int TPP = 256 / CPR;                       // tokens per pass
-  const int sc = tid % CPR;
-  const int sj = tid / CPR;
-  i32x4 st[PASSES];
+  // ---- key block staging into LDS buffer `buf` -------------------------
+  // LDS layout: token jj's 16-byte chunk c sits at jj*RB + ((c ^ swz(jj)) << 4)
+  // with swz(jj) = jj & 15 (256-byte rows) or (jj >> 1) & 7 (128-byte rows),
+  // so the 32 tokens an MFMA operand read touches hit distinct banks.
+  // fp16/bf16/fp8: each wave instruction copies 1 KB straight from HBM/L2 into
+  // LDS (global_load_lds, no registers); LDS receives lane l's 16 bytes at
+  // base + 16*l, so the swizzle is applied to the global address instead.
+  // int8: loaded to registers, widened to fp16, written with the swizzle.
+  i32x4 st[4];
   float sv = 0.f;
-
-  auto gload = [&](int beta) {
+  auto stage_async = [&](int beta, int buf) {
+    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
+    const int nvalid = min(kP, w.L - beta * kP);
+    constexpr int RPI = 1024 / RB;                  // tokens per wave instruction
+    constexpr int NI = BUF / 1024 / 4;              // wave instructions per wave
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int X = wave * NI + q;
+      const int jj = X * RPI + l / (RB / 16);
+      const int pos = l % (RB / 16);
+      const int c = pos ^ (RB == 256 ? (jj & 15) : ((jj >> 1) & 7));
+      if (jj < nvalid) {
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(kb + (int64_t)jj * p.k_row_stride + 16 * c),
+            (__attribute__((address_space(3))) void*)(kl + buf * BUF + X * 1024),
+            16, 0, 0);
+      }
+    }
+  };
+  auto gload_i8 = [&](int beta) {
     const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int jj = ps * TPP + sj;
-      st[ps] = (jj < nvalid) ? ld16(kb + (int64_t)jj * p.k_row_stride + 16 * sc)
+    for (int ps = 0; ps < 4; ++ps) {
+      const int jj = ps * 32 + (tid >> 3);
+      st[ps] = (jj < nvalid) ? ld16(kb + (int64_t)jj * p.k_row_stride + 16 * (tid & 7))
                              : i32x4{0, 0, 0, 0};
     }
-    if constexpr (Kd::is_i8) {
-      if (tid < kP)
-        sv = (tid < nvalid)
-                 ? p.scale[scale_offset(p, w, beta, w.hk) + (int64_t)tid * p.s_row_stride]
-                 : 0.f;
-    }
+    if (tid < kP)
+      sv = (tid < nvalid)
+               ? p.scale[scale_offset(p, w, beta, w.hk) + (int64_t)tid * p.s_row_stride]
+               : 0.f;
   };
-  auto lstore = [&]() {
+  auto lstore_i8 = [&](int buf) {
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int jj = ps * TPP + sj;
-      if constexpr (Kd::is_f8) {
-        *reinterpret_cast<i32x4*>(kl + jj * 128 + ((sc ^ ((jj >> 1) & 7)) << 4)) = st[ps];
-      } else if constexpr (Kd::is_i8) {
-        i32x4 a, b;
-        i8x16_to_f16x16(st[ps], a, b);
-        *reinterpret_cast<i32x4*>(kl + jj * 256 + (((2 * sc) ^ (jj & 15)) << 4)) = a;
-        *reinterpret_cast<i32x4*>(kl + jj * 256 + (((2 * sc + 1) ^ (jj & 15)) << 4)) = b;
-      } else {
-        *reinterpret_cast<i32x4*>(kl + jj * 256 + ((sc ^ (jj & 15)) << 4)) = st[ps];
-      }
+    for (int ps = 0; ps < 4; ++ps) {
+      const int jj = ps * 32 + (tid >> 3);
+      const int sc = tid & 7;
+      i32x4 a, b;
+      i8x16_to_f16x16(st[ps], a, b);
+      uint8_t* row = kl + buf * BUF + jj * 256;
+      *reinterpret_cast<i32x4*>(row + (((2 * sc) ^ (jj & 15)) << 4)) = a;
+      *reinterpret_cast<i32x4*>(row + (((2 * sc + 1) ^ (jj & 15)) << 4)) = b;
     }
-    if constexpr (Kd::is_i8) {
-      if (tid < kP) scl[tid] = sv;
-    }
+    if (tid < kP) scl[buf][tid] = sv;
   };
 
-  if (w.c0 < vend) gload(w.c0);
+  // the row this lane writes at the end (after the cross-half reduction,
+  // lanes of group 0 hold N tile 0's rows and group 1 N tile 1's)
+  float resv[kPrefillChunk];
+#pragma unroll
+  for (int k = 0; k < kPrefillChunk; ++k) resv[k] = -__builtin_inff();
+
+  if (busy) {
+    if constexpr (Kd::is_i8) {
+      gload_i8(w.c0);
+      lstore_i8(0);
+    } else {
+      stage_async(w.c0, 0);
+    }
+  }
   for (int beta = w.c0; beta < vend; ++beta) {
+    const int cur = (beta - w.c0) & 1;
+    // the current block has landed in LDS and every wave is done with the
+    // other buffer, which the next block may now overwrite
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    lstore();
-    __syncthreads();
-    if (beta + 1 < vend) gload(beta + 1);
-
-    const bool full = beta * kP + kP - 1 <= lim_lo;
-    float run0 = -__builtin_inff(), run1 = -__builtin_inff();
-#pragma unroll 1
-    for (int mt = 0; mt < 4; ++mt) {
-      const int jj = mt * 32 + n;
-      f32x16 acc0 = {}, acc1 = {};
-      if constexpr (Kd::is_f8) {
-        const int sw = (jj >> 1) & 7;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int c = 4 * s + 2 * G;
-          const i32x4 a0 = *reinterpret_cast<const i32x4*>(kl + jj * 128 + ((c ^ sw) << 4));
-          const i32x4 a1 = *reinterpret_cast<const i32x4*>(kl + jj * 128 + (((c + 1) ^ sw) << 4));
-          const i32x8 a = cat(a0, a1);
-          acc0 = mfma32x32x64_f8<KK>(a, cat(qv[0][2 * s], qv[0][2 * s + 1]), acc0);
-          acc1 = mfma32x32x64_f8<KK>(a, cat(qv[1][2 * s], qv[1][2 * s + 1]), acc1);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int c = 2 * s + G;
-          const i32x4 a = *reinterpret_cast<const i32x4*>(kl + jj * 256 + ((c ^ (jj & 15)) << 4));
-          acc0 = mfma32x32x16<Kd::mfma_kind>(a, qv[0][s], acc0);
-          acc1 = mfma32x32x16<Kd::mfma_kind>(a, qv[1][s], acc1);
-        }
-      }
-      // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
-        float v0 = acc0[r], v1 = acc1[r];
-        if constexpr (Kd::is_i8) {
-          const float s = scl[jr];
-          v0 *= s;
-          v1 *= s;
-        }
-        if (!full) {
-          const int j = beta * kP + jr;
-          v0 = (j <= lim[0]) ? v0 : -__builtin_inff();
-          v1 = (j <= lim[1]) ? v1 : -__builtin_inff();
-        }
-        run0 = fmaxf(run0, v0);
-        run1 = fmaxf(run1, v1);
-      }
+    const bool more = beta + 1 < vend;
+    if (more) {
+      if constexpr (Kd::is_i8)
+        gload_i8(beta + 1);
+      else
+        stage_async(beta + 1, cur ^ 1);
     }
+    const uint8_t* kc = kl + cur * BUF;
+
+    float run0 = -__builtin_inff(), run1 = -__builtin_inff();
+    // One pass over the block's four 32-token M tiles; MASKED selects -inf for
+    // key tokens past each row's last visible one (only blocks cut by the
+    // window or by kv_len need it).  The branch below is uniform per block.
+    auto block = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int jj = mt * 32 + n;
+        f32x16 acc0 = {}, acc1 = {};
+        if constexpr (Kd::is_f8) {
+          const int sw = (jj >> 1) & 7;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int c = 4 * s + 2 * G;
+            const i32x4 a0 = *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ sw) << 4));
+            const i32x4 a1 =
+                *reinterpret_cast<const i32x4*>(kc + jj * 128 + (((c + 1) ^ sw) << 4));
+            const i32x8 a = cat(a0, a1);
+            acc0 = mfma32x32x64_f8<KK>(a, cat(qv[0][2 * s], qv[0][2 * s + 1]), acc0);
+            acc1 = mfma32x32x64_f8<KK>(a, cat(qv[1][2 * s], qv[1][2 * s + 1]), acc1);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const int c = 2 * s + G;
+            const i32x4 a =
+                *reinterpret_cast<const i32x4*>(kc + jj * 256 + ((c ^ (jj & 15)) << 4));
+            acc0 = mfma32x32x16<Kd::mfma_kind>(a, qv[0][s], acc0);
+            acc1 = mfma32x32x16<Kd::mfma_kind>(a, qv[1][s], acc1);
+          }
+        }
+        // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+          float v0 = acc0[r], v1 = acc1[r];
+          if constexpr (Kd::is_i8) {
+            const float sc = scl[cur][jr];
+            v0 *= sc;
+            v1 *= sc;
+          }
+          if constexpr (MASKED) {
+            const int j = beta * kP + jr;
+            v0 = (j <= lim[0]) ? v0 : -__builtin_inff();
+            v1 = (j <= lim[1]) ? v1 : -__builtin_inff();
+          }
+          run0 = fmaxf(run0, v0);
+          run1 = fmaxf(run1, v1);
+        }
+      }
+    };
+    if (beta * kP + kP - 1 <= lim_lo)
+      block(std::false_type{});
+    else
+      block(std::true_type{});
+
     // the two k groups hold the two halves of each 32-token M tile
     run0 = fmaxf(run0, __shfl_xor(run0, 32, 64));
     run1 = fmaxf(run1, __shfl_xor(run1, 32, 64));
-    res[wave * 64 + G * 32 + n][beta - w.c0] = G ? run1 : run0;
-  }
-  __syncthreads();
+    const float v = G ? run1 : run0;
+    const int kk = beta - w.c0;
+#pragma unroll
+    for (int k = 0; k < kPrefillChunk; ++k) resv[k] = (k == kk) ? v : resv[k];
 
-  // one thread per row writes the row's columns [c0, c1)
-  const int r = tid;
+    if constexpr (Kd::is_i8) {
+      if (more) lstore_i8(cur ^ 1);
+    }
+  }
+
+  // each lane writes its row's columns [c0, c1)
+  const int r = wave * 64 + G * 32 + n;
   const int ti = r / p.hpt;
   const int hg = w.hc * p.hpt + (r - ti * p.hpt);
   if (r < p.hpt * p.tpt && ti < w.ntok && hg < p.g) {
@@ -549,14 +604,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
     const int64_t h = (int64_t)w.hk * p.g + hg;
     float* o = p.out + (h * p.T + (w.t0 + ti)) * p.W + w.c0;
     const int cols = w.c1 - w.c0;   // a multiple of 4: W and c0 are multiples of 16
-    for (int c = 0; c < cols; c += 4) {
-      f32x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int beta = w.c0 + c + e;
-        v[e] = finish(p, w.L, start, beta, beta < vend, res[r][c + e]);
+    for (int c = 0; c < kPrefillChunk; c += 4) {
+      if (c < cols) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int beta = w.c0 + c + e;
+          v[e] = finish(p, w.L, start, beta, beta < vend, resv[c + e]);
+        }
+        *reinterpret_cast<f32x4*>(o + c) = v;
       }
-      *reinterpret_cast<f32x4*>(o + c) = v;
     }
   }
 }
