@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
 // ---------------------------------------------------------------------------
 
 template <int KK>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
+__global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(Params p) {
   using Kd = Kind<KK>;
   // bytes per key token in LDS: fp8 stays fp8, int8 is widened to fp16
   constexpr int RB = Kd::is_f8 ? 128 : 256;
@@ -531,50 +531,72 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Params p) {
     // window or by kv_len need it).  The branch below is uniform per block.
     auto block = [&](auto masked) {
       constexpr bool MASKED = decltype(masked)::value;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      // Key fragments (MFMA A operand), 16 bytes each, in the order they are
+      // consumed: M tile mt (32 tokens), k step s, and for fp8 the two halves
+      // of a 32-byte operand.  Fragment i + LEAD is read from LDS while
+      // fragment i feeds the MFMAs, which hides the LDS latency with only
+      // LEAD + 1 fragments live.
+      constexpr int PER_MT = Kd::is_f8 ? 4 : 8; // fragments per M tile
+      constexpr int NFR = 4 * PER_MT;
+      constexpr int LEAD = 4;
+      auto frag = [&](int i) -> i32x4 {
+        const int mt = i / PER_MT, q = i % PER_MT;
         const int jj = mt * 32 + n;
-        f32x16 acc0 = {}, acc1 = {};
         if constexpr (Kd::is_f8) {
-          const int sw = (jj >> 1) & 7;
+          // q = 2*s + half: bytes [64s + 32G + 16*half, +16) of the token
+          const int c = 4 * (q >> 1) + 2 * G + (q & 1);
+          return *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ ((jj >> 1) & 7)) << 4));
+        } else {
+          const int c = 2 * q + G;
+          return *reinterpret_cast<const i32x4*>(kc + jj * 256 + ((c ^ (jj & 15)) << 4));
+        }
+      };
+      i32x4 f[NFR];
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int c = 4 * s + 2 * G;
-            const i32x4 a0 = *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ sw) << 4));
-            const i32x4 a1 =
-                *reinterpret_cast<const i32x4*>(kc + jj * 128 + (((c + 1) ^ sw) << 4));
-            const i32x8 a = cat(a0, a1);
+      for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int i = 0; i < NFR; ++i) {
+        if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
+        const int mt = i / PER_MT, q = i % PER_MT;
+        if (q == 0) {
+          acc0 = f32x16{};
+          acc1 = f32x16{};
+        }
+        if constexpr (Kd::is_f8) {
+          if (q & 1) {
+            const int s = q >> 1;
+            const i32x8 a = cat(f[i - 1], f[i]);
             acc0 = mfma32x32x64_f8<KK>(a, cat(qv[0][2 * s], qv[0][2 * s + 1]), acc0);
             acc1 = mfma32x32x64_f8<KK>(a, cat(qv[1][2 * s], qv[1][2 * s + 1]), acc1);
           }
         } else {
+          acc0 = mfma32x32x16<Kd::mfma_kind>(f[i], qv[0][q], acc0);
+          acc1 = mfma32x32x16<Kd::mfma_kind>(f[i], qv[1][q], acc1);
+        }
+        if (q == PER_MT - 1) {
+          // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
 #pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const int c = 2 * s + G;
-            const i32x4 a =
-                *reinterpret_cast<const i32x4*>(kc + jj * 256 + ((c ^ (jj & 15)) << 4));
-            acc0 = mfma32x32x16<Kd::mfma_kind>(a, qv[0][s], acc0);
-            acc1 = mfma32x32x16<Kd::mfma_kind>(a, qv[1][s], acc1);
+          for (int r = 0; r < 16; ++r) {
+            const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+            float v0 = acc0[r], v1 = acc1[r];
+            if constexpr (Kd::is_i8) {
+              const float sc = scl[cur][jr];
+              v0 *= sc;
+              v1 *= sc;
+            }
+            if constexpr (MASKED) {
+              const int j = beta * kP + jr;
+              v0 = (j <= lim[0]) ? v0 : -__builtin_inff();
+              v1 = (j <= lim[1]) ? v1 : -__builtin_inff();
+            }
+            run0 = fmaxf(run0, v0);
+            run1 = fmaxf(run1, v1);
           }
         }
-        // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
-          float v0 = acc0[r], v1 = acc1[r];
-          if constexpr (Kd::is_i8) {
-            const float sc = scl[cur][jr];
-            v0 *= sc;
-            v1 *= sc;
-          }
-          if constexpr (MASKED) {
-            const int j = beta * kP + jr;
-            v0 = (j <= lim[0]) ? v0 : -__builtin_inff();
-            v1 = (j <= lim[1]) ? v1 : -__builtin_inff();
-          }
-          run0 = fmaxf(run0, v0);
-          run1 = fmaxf(run1, v1);
-        }
+        // keep this shape: one fragment read, its MFMAs, (an epilogue); the
+        // compiler would otherwise hoist every read and run out of registers
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (beta * kP + kP - 1 <= lim_lo)
