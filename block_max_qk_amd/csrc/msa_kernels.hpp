@@ -386,12 +386,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
 // ---------------------------------------------------------------------------
 
 template <int KK>
-__global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(Params p) {
+__global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(Params p) {
   using Kd = Kind<KK>;
-  // bytes per key token in LDS: fp8 stays fp8, int8 is widened to fp16
-  constexpr int RB = Kd::is_f8 ? 128 : 256;
-  constexpr int BUF = kP * RB;                 // one key block in LDS
-  __shared__ __attribute__((aligned(16))) uint8_t kl[2 * BUF];
+  // Key blocks pass through an LDS ring of stages.  16-bit keys: stages of 64
+  // tokens (16 KB), three deep, so a stage's copy has two compute periods to
+  // land; fp8: whole 128-token blocks (16 KB), two deep; int8 (widened to
+  // fp16 through registers): whole blocks (32 KB), two deep.  All of it fits
+  // three workgroups per CU (two for int8).
+  constexpr int RB = Kd::is_f8 ? 128 : 256;    // LDS bytes per key token
+  constexpr bool ASYNC = !Kd::is_i8;           // copy HBM/L2 -> LDS directly
+  constexpr int ST = (ASYNC && RB == 256) ? 64 : kP;   // tokens per stage
+  constexpr int SPB = kP / ST;                 // stages per block
+  constexpr int RING = SPB == 2 ? 3 : 2;
+  constexpr int SBYTES = ST * RB;
+  constexpr int NI = SBYTES / 1024 / 4;        // copy instructions per wave per stage
+  static_assert(!ASYNC || NI == 4, "the ring's wait counts assume four copies per wave per stage");
+  __shared__ __attribute__((aligned(16))) uint8_t kl[RING * SBYTES];
   __shared__ float scl[2][kP];
 
   const Work w = locate(p);
@@ -447,29 +457,47 @@ __global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(P
   // LDS (global_load_lds, no registers); LDS receives lane l's 16 bytes at
   // base + 16*l, so the swizzle is applied to the global address instead.
   // int8: loaded to registers, widened to fp16, written with the swizzle.
+  // page indices of the work item's blocks, one per lane, read with readlane
+  int pidx = 0;
+  if (p.paged && busy && l < vend - w.c0) pidx = p.block_table[(int64_t)w.b * p.MB + w.c0 + l];
+  auto block_bytes = [&](int beta) -> int64_t {
+    if (p.paged) return (int64_t)__builtin_amdgcn_readlane(pidx, beta - w.c0) * p.k_page_stride;
+    return (w.koff + (int64_t)beta * kP) * p.k_row_stride;
+  };
+  auto block_scale = [&](int beta) -> int64_t {
+    if (p.paged)
+      return (int64_t)__builtin_amdgcn_readlane(pidx, beta - w.c0) * p.s_page_stride +
+             (int64_t)w.hk * p.s_head_stride;
+    return (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)w.hk * p.s_head_stride;
+  };
+
   i32x4 st[4];
   float sv = 0.f;
-  auto stage_async = [&](int beta, int buf) {
-    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
+  // stage sg (block c0 + sg/SPB, tokens [off, off+ST)) into ring slot `slot`;
+  // always exactly NI copy instructions per wave (the ring's waits count
+  // them): token rows at or past kv_len copy row 0 of the block instead, which
+  // the masked path discards
+  auto stage_async = [&](int sg, int slot, int64_t kbytes) {
+    const int beta = w.c0 + sg / SPB;
+    const int off = (sg % SPB) * ST;
+    const uint8_t* kb = p.k + kbytes + (int64_t)w.hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
-    constexpr int RPI = 1024 / RB;                  // tokens per wave instruction
-    constexpr int NI = BUF / 1024 / 4;              // wave instructions per wave
+    constexpr int RPI = 1024 / RB;                  // tokens per copy instruction
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const int X = wave * NI + q;
-      const int jj = X * RPI + l / (RB / 16);
+      const int jl = X * RPI + l / (RB / 16);       // token within the stage
       const int pos = l % (RB / 16);
-      const int c = pos ^ (RB == 256 ? (jj & 15) : ((jj >> 1) & 7));
-      if (jj < nvalid) {
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(kb + (int64_t)jj * p.k_row_stride + 16 * c),
-            (__attribute__((address_space(3))) void*)(kl + buf * BUF + X * 1024),
-            16, 0, 0);
-      }
+      const int c = pos ^ (RB == 256 ? (jl & 15) : ((jl >> 1) & 7));
+      const int jj = off + jl;
+      const int src = jj < nvalid ? jj : 0;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(kb + (int64_t)src * p.k_row_stride + 16 * c),
+          (__attribute__((address_space(3))) void*)(kl + slot * SBYTES + X * 1024), 16, 0, 0);
     }
   };
   auto gload_i8 = [&](int beta) {
-    const uint8_t* kb = p.k + block_offset(p, w, beta) + (int64_t)w.hk * p.k_head_stride;
+    const uint8_t* kb = p.k + block_bytes(beta) + (int64_t)w.hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
@@ -478,54 +506,100 @@ __global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(P
                              : i32x4{0, 0, 0, 0};
     }
     if (tid < kP)
-      sv = (tid < nvalid)
-               ? p.scale[scale_offset(p, w, beta, w.hk) + (int64_t)tid * p.s_row_stride]
-               : 0.f;
+      sv = (tid < nvalid) ? p.scale[block_scale(beta) + (int64_t)tid * p.s_row_stride] : 0.f;
   };
-  auto lstore_i8 = [&](int buf) {
+  auto lstore_i8 = [&](int slot) {
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
       const int jj = ps * 32 + (tid >> 3);
       const int sc = tid & 7;
       i32x4 a, b;
       i8x16_to_f16x16(st[ps], a, b);
-      uint8_t* row = kl + buf * BUF + jj * 256;
+      uint8_t* row = kl + slot * SBYTES + jj * 256;
       *reinterpret_cast<i32x4*>(row + (((2 * sc) ^ (jj & 15)) << 4)) = a;
       *reinterpret_cast<i32x4*>(row + (((2 * sc + 1) ^ (jj & 15)) << 4)) = b;
     }
-    if (tid < kP) scl[buf][tid] = sv;
+    if (tid < kP) scl[slot][tid] = sv;
   };
 
-  // the row this lane writes at the end (after the cross-half reduction,
-  // lanes of group 0 hold N tile 0's rows and group 1 N tile 1's)
-  float resv[kPrefillChunk];
-#pragma unroll
-  for (int k = 0; k < kPrefillChunk; ++k) resv[k] = -__builtin_inff();
+  // The output row this lane writes: after the cross-half reduction, lanes of
+  // k group 0 hold N tile 0's rows and group 1 N tile 1's.  Each block's
+  // result is stored as soon as it is known (the L2 merges a row's columns).
+  const int orow = wave * 64 + G * 32 + n;
+  const int oti = orow / p.hpt;
+  const int ohg = w.hc * p.hpt + (orow - oti * p.hpt);
+  const bool orow_ok = orow < p.hpt * p.tpt && oti < w.ntok && ohg < p.g;
+  float* const orow_ptr =
+      p.out + (((int64_t)w.hk * p.g + ohg) * p.T + (w.t0 + oti)) * p.W;
+  const int ostart = p.start_loc[w.b];
 
-  if (busy) {
-    if constexpr (Kd::is_i8) {
+  const int nst = busy ? (vend - w.c0) * SPB : 0;   // stages of this work item
+  if constexpr (ASYNC) {
+    // the first block's page index is read before any copy is in flight
+    const int64_t kb0 = nst > 0 ? block_bytes(w.c0) : 0;
+#pragma unroll
+    for (int sg = 0; sg < RING - 1; ++sg)
+      if (sg < nst) stage_async(sg, sg, sg < SPB ? kb0 : block_bytes(w.c0 + sg / SPB));
+  } else {
+    if (nst > 0) {
       gload_i8(w.c0);
       lstore_i8(0);
-    } else {
-      stage_async(w.c0, 0);
     }
   }
-  for (int beta = w.c0; beta < vend; ++beta) {
-    const int cur = (beta - w.c0) & 1;
-    // the current block has landed in LDS and every wave is done with the
-    // other buffer, which the next block may now overwrite
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = beta + 1 < vend;
-    if (more) {
-      if constexpr (Kd::is_i8)
-        gload_i8(beta + 1);
-      else
-        stage_async(beta + 1, cur ^ 1);
+  float run0 = -__builtin_inff(), run1 = -__builtin_inff();
+  // Block results of this lane's row collect in registers, RG blocks at a
+  // time, and are written as RG consecutive floats (16-byte stores).  16-bit
+  // keys run at the register limit and flush every 4 blocks; fp8 and int8
+  // once per work item.
+  constexpr int RG = (ASYNC && RB == 256) ? 4 : kPrefillChunk;
+  float resv[RG];
+  int pend = -1;                 // first block of a group waiting to be written
+  auto flush = [&](int g0) {
+    if (orow_ok) {
+#pragma unroll
+      for (int c = 0; c < RG; c += 4) {
+        if (g0 + c < w.c1) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int beta = g0 + c + e;
+            v[e] = finish(p, w.L, ostart, beta, beta < vend, resv[c + e]);
+          }
+          *reinterpret_cast<f32x4*>(orow_ptr + g0 + c) = v;
+        }
+      }
     }
-    const uint8_t* kc = kl + cur * BUF;
-
-    float run0 = -__builtin_inff(), run1 = -__builtin_inff();
+  };
+  for (int sg = 0; sg < nst; ++sg) {
+    const int slot = sg % RING;
+    const int beta = w.c0 + sg / SPB;
+    const int off = (sg % SPB) * ST;
+    // Stage sg has landed (the one copy still allowed in flight is the next
+    // stage's) and every wave is done with the slot the copy below reuses.
+    // Written out because a plain __syncthreads() would wait for all copies.
+    if (RING == 3 && sg + 1 < nst)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // a finished group of results is written here, ahead of the next
+    // copies, so that the copies stay the newest memory operations the
+    // waits count
+    if (pend >= 0) {
+      flush(pend);
+      pend = -1;
+    }
+    if (sg + RING - 1 < nst) {
+      if constexpr (ASYNC)
+        stage_async(sg + RING - 1, (sg + RING - 1) % RING,
+                    block_bytes(w.c0 + (sg + RING - 1) / SPB));
+      else
+        gload_i8(beta + 1);
+    }
+    const uint8_t* kc = kl + slot * SBYTES;
+    if (off == 0) {
+      run0 = -__builtin_inff();
+      run1 = -__builtin_inff();
+    }
     // One pass over the block's four 32-token M tiles; MASKED selects -inf for
     // key tokens past each row's last visible one (only blocks cut by the
     // window or by kv_len need it).  The branch below is uniform per block.
@@ -537,8 +611,8 @@ __global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(P
       // fragment i feeds the MFMAs, which hides the LDS latency with only
       // LEAD + 1 fragments live.
       constexpr int PER_MT = Kd::is_f8 ? 4 : 8; // fragments per M tile
-      constexpr int NFR = 4 * PER_MT;
-      constexpr int LEAD = 4;
+      constexpr int NFR = (ST / 32) * PER_MT;
+      constexpr int LEAD = Kd::is_f8 ? 4 : 2;
       auto frag = [&](int i) -> i32x4 {
         const int mt = i / PER_MT, q = i % PER_MT;
         const int jj = mt * 32 + n;
@@ -578,10 +652,10 @@ __global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(P
           // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+            const int jr = off + mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
             float v0 = acc0[r], v1 = acc1[r];
             if constexpr (Kd::is_i8) {
-              const float sc = scl[cur][jr];
+              const float sc = scl[slot][jr];
               v0 *= sc;
               v1 *= sc;
             }
@@ -604,39 +678,30 @@ __global__ __launch_bounds__(256, Kind<KK>::is_f8 ? 3 : 2) void prefill_kernel(P
     else
       block(std::true_type{});
 
-    // the two k groups hold the two halves of each 32-token M tile
-    run0 = fmaxf(run0, __shfl_xor(run0, 32, 64));
-    run1 = fmaxf(run1, __shfl_xor(run1, 32, 64));
-    const float v = G ? run1 : run0;
-    const int kk = beta - w.c0;
+    if (off + ST == kP) {
+      // the two k groups hold the two halves of each 32-token M tile
+      run0 = fmaxf(run0, __shfl_xor(run0, 32, 64));
+      run1 = fmaxf(run1, __shfl_xor(run1, 32, 64));
+      const float v = G ? run1 : run0;
+      const int kk = (beta - w.c0) % RG;
 #pragma unroll
-    for (int k = 0; k < kPrefillChunk; ++k) resv[k] = (k == kk) ? v : resv[k];
-
-    if constexpr (Kd::is_i8) {
-      if (more) lstore_i8(cur ^ 1);
+      for (int k = 0; k < RG; ++k) resv[k] = (k == kk) ? v : resv[k];
+      if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
+    }
+    if constexpr (!ASYNC) {
+      if (sg + 1 < nst) lstore_i8(slot ^ 1);
     }
   }
 
-  // each lane writes its row's columns [c0, c1)
-  const int r = wave * 64 + G * 32 + n;
-  const int ti = r / p.hpt;
-  const int hg = w.hc * p.hpt + (r - ti * p.hpt);
-  if (r < p.hpt * p.tpt && ti < w.ntok && hg < p.g) {
-    const int start = p.start_loc[w.b];
-    const int64_t h = (int64_t)w.hk * p.g + hg;
-    float* o = p.out + (h * p.T + (w.t0 + ti)) * p.W + w.c0;
-    const int cols = w.c1 - w.c0;   // a multiple of 4: W and c0 are multiples of 16
+  if (pend >= 0) flush(pend);
+  // columns of the work item past the last group: -inf and local_mask
+  if (orow_ok) {
+    const int done = busy ? w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG : w.c0;
+    for (int beta = done; beta < w.c1; beta += 4) {
+      f32x4 v;
 #pragma unroll
-    for (int c = 0; c < kPrefillChunk; c += 4) {
-      if (c < cols) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int beta = w.c0 + c + e;
-          v[e] = finish(p, w.L, start, beta, beta < vend, resv[c + e]);
-        }
-        *reinterpret_cast<f32x4*>(o + c) = v;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, ostart, beta + e, false, 0.f);
+      *reinterpret_cast<f32x4*>(orow_ptr + beta) = v;
     }
   }
 }
