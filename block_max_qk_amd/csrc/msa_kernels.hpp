@@ -33,7 +33,7 @@ namespace msa {
 
 constexpr int kDecodeRows = 16;
 constexpr int kPrefillRows = 256;
-constexpr int kPrefillChunk = 16;
+constexpr int kPrefillChunk = 16;   // blocks per prefill work item (fp8: twice that)
 
 // ---------------------------------------------------------------------------
 // decode
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
   // time, and are written as RG consecutive floats (16-byte stores).  16-bit
   // keys run at the register limit and flush every 4 blocks; fp8 and int8
   // once per work item.
-  constexpr int RG = (ASYNC && RB == 256) ? 4 : kPrefillChunk;
+  constexpr int RG = (ASYNC && RB == 256) ? 4 : 16;
   float resv[RG];
   int pend = -1;                 // first block of a group waiting to be written
   auto flush = [&](int g0) {
