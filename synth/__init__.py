@@ -11,6 +11,7 @@ from .inputs import (  # noqa: F401
     config_case,
     make_case,
     edge_cases,
+    random_cases,
     poison_case,
     case_summary,
 )

@@ -433,7 +433,44 @@ def edge_cases() -> List[MsaCase]:
         kdtype="i8", layout="BNBD", extra_pages=5, init_blocks=0, local_blocks=1)
     add("prefill_bbnd_f16_g16", q_lens=[64, 40], kv_lens=[64, 300], Hq=16, Hkv=1,
         qdtype="f16", layout="BBND", extra_pages=6)
+    # fp8 e5m2 (same kernels, the other OCP operand format)
+    add("mix_bbnd_f8e5m2", q_lens=[3, 1, 37], kv_lens=[300, 129, 600], Hq=8, Hkv=2,
+        qdtype="f8e5m2", layout="BBND", extra_pages=4, init_blocks=1, local_blocks=2)
+    add("prefill_tnd_f8e5m2", q_lens=[130], kv_lens=[400], Hq=16, Hkv=2, qdtype="f8e5m2",
+        layout="TND", init_blocks=1, local_blocks=1)
     return cs
+
+
+def random_cases(n: int, seed: int = 4242) -> List[MsaCase]:
+    """n small cases with every knob drawn at random (lengths, heads, key type,
+    layout, mode, local_mask counts, table width, dim0 gap), for sweeps."""
+    rng = np.random.default_rng(seed)
+    pairs = [("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("f8e4m3", "f8e4m3"),
+             ("f8e5m2", "f8e5m2")]
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 6))
+        q_lens = [int(x) for x in rng.choice([0, 1, 2, 3, 5, 17, 40, 90], size=B)]
+        kv_lens = [int(x) for x in rng.choice([0, 1, 100, 127, 128, 129, 300, 511, 700],
+                                               size=B)]
+        Hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 3, 8, 16, 20]))
+        qd, kd = pairs[int(rng.integers(len(pairs)))]
+        layout = str(rng.choice(["BBND", "BNBD", "TND"]))
+        mode = int(rng.choice([0, 3]))
+        nb = max(1, max(-(-k // 128) for k in kv_lens))
+        MB = None if layout == "TND" else nb + int(rng.integers(0, 20))
+        limit = (MB if MB is not None else ((nb + 15) // 16) * 16)
+        init = int(rng.integers(0, min(3, limit) + 1))
+        local = int(rng.integers(0, min(3, limit) + 1))
+        starts = [int(rng.integers(0, MB if MB is not None else nb)) for _ in range(B)]
+        gap = int(rng.choice([0, 0, 1])) if layout != "TND" else 0
+        out.append(make_case(f"rand{i}_{layout.lower()}_{kd}_g{g}", seed + 1 + i,
+                             q_lens=q_lens, kv_lens=kv_lens, Hq=Hkv * g, Hkv=Hkv, qdtype=qd,
+                             kdtype=kd, layout=layout, MB=MB, extra_pages=int(rng.integers(0, 4)),
+                             gap=gap, sparse_mode=mode, init_blocks=init, local_blocks=local,
+                             start_loc=starts))
+    return out
 
 
 def case_summary(case: MsaCase) -> dict:

@@ -121,6 +121,15 @@ def test_brute_force_agreement(idx):
     assert_close_ulp(oracle.index_score_case(c), brute_force(c))
 
 
+RANDOM = synth.random_cases(40)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM)), ids=[c.name for c in RANDOM])
+def test_brute_force_agreement_random(idx):
+    c = RANDOM[idx]
+    assert_close_ulp(oracle.index_score_case(c), brute_force(c))
+
+
 # ---------------------------------------------------------------------------
 # closed forms of the causal window
 # ---------------------------------------------------------------------------

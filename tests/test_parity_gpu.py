@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 
 EDGE = synth.edge_cases()
 PAGED = [c for c in EDGE if c.layout != "TND"]
+RANDOM = synth.random_cases(40)
 
 
 def log(*a):
@@ -82,6 +83,15 @@ def test_edge_case_parity(idx, family, dev):
     ref = oracle_out(c)
     got = run_gpu(c, dev, family)
     r = check(ref, got, tol_of(c))
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("family", [0, 1])
+@pytest.mark.parametrize("idx", range(len(RANDOM)), ids=[c.name for c in RANDOM])
+def test_random_sweep_parity(idx, family, dev):
+    c = RANDOM[idx]
+    log(f"[gpu] random {c.name} family={family} {synth.case_summary(c)}")
+    r = check(oracle_out(c), run_gpu(c, dev, family), tol_of(c))
     assert r["ok"], r
 
 
