@@ -260,8 +260,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the operator has no cross-GPU step here "
-              "(see the sharding notes in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: every block score is independent, so the "
+              "operator shards across GPUs with no exchange and there is no multi-GPU step "
+              "to time; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

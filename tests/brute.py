@@ -1,7 +1,7 @@
 """Vectorised brute force for the block score, used only to pin the oracle.
 
 It follows the block-selection sketch of the DSA forward-path notes (section
-3, "从 token score 得到 block Selection"): full token scores, ``masked_fill``
+3, from token scores to block selection): full token scores, ``masked_fill``
 of every invisible position with -inf, ``reshape`` into blocks of P tokens and
 ``amax`` over each block; then the local_mask constants of the msa_index_score
 guide (section 二).  Inputs are decoded with torch's own ``.to(float64)`` and
