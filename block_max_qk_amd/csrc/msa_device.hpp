@@ -93,10 +93,13 @@ __device__ __forceinline__ i32x4 ld16_stream(const uint8_t* p) {
 // A work item is (unit, tile): a unit is (KV head, head chunk, block chunk),
 // a tile is `tpt` consecutive query tokens of one request.  The hardware
 // hands workgroups to the eight XCDs round-robin by workgroup id, so the id is
-// remapped such that each XCD receives whole units and walks their tiles in
-// order: workgroups that run together on one XCD then read the same key
-// blocks through that XCD's L2, and the units (block ranges of very different
-// cost under the causal window) are dealt across XCDs in turn.
+// remapped such that each XCD walks runs of eight consecutive tiles of one
+// unit: the workgroups of a run start together and read the same key blocks
+// through that XCD's L2.  Successive runs of a unit go to successive XCDs,
+// which deals every unit's work over all eight.  (Keeping each unit on one
+// XCD would give the most L2 reuse, but under the causal window low block
+// chunks carry far more work than high ones, and the XCDs holding them would
+// finish last.)
 // ---------------------------------------------------------------------------
 
 struct Work {
@@ -115,7 +118,7 @@ __device__ __forceinline__ Work locate(const Params& p) {
   const int slot = bid >> 3;
   const int ui = slot / p.ntiles;
   const int tile = slot - ui * p.ntiles;
-  const int unit = ui * 8 + xcd;
+  const int unit = ui * 8 + ((xcd + tile / 8) & 7);
   if (unit >= p.units) return w;
   w.hk = unit / (p.hchunks * p.nchunks);
   const int rem = unit - w.hk * (p.hchunks * p.nchunks);
@@ -170,25 +173,6 @@ __device__ __forceinline__ Work locate(const Params& p) {
 __device__ __forceinline__ int last_visible(const Params& p, const Work& w, int i) {
   const int qpos = p.causal ? (w.L - w.Lq + i) : (w.L - 1);
   return min(qpos, w.L - 1);
-}
-
-// Byte offset of key block `beta` of the work item's request (head 0).
-__device__ __forceinline__ int64_t block_offset(const Params& p, const Work& w, int beta) {
-  if (p.paged) {
-    const int64_t page = p.block_table[(int64_t)w.b * p.MB + beta];
-    return page * p.k_page_stride;
-  }
-  return (w.koff + (int64_t)beta * kP) * p.k_row_stride;
-}
-
-// Scale element index of token 0 of block `beta`, head hk.
-__device__ __forceinline__ int64_t scale_offset(const Params& p, const Work& w, int beta,
-                                                int hk) {
-  if (p.paged) {
-    const int64_t page = p.block_table[(int64_t)w.b * p.MB + beta];
-    return page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
-  }
-  return (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
 }
 
 // Final value of output column beta of a row (after the block maximum `v`

@@ -191,7 +191,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   // plan
   const int32_t g = (int32_t)(Hq / Hkv);
   const int fam = family >= 0 ? family : choose_family(T, batch, g);
-  const int rows = fam == 1 ? msa::kPrefillRows : msa::kDecodeRows;
+  const int rows = fam == 1 ? msa::prefill_rows(key->dtype) : msa::kDecodeRows;
   Params p{};
   p.q = static_cast<const uint8_t*>(query->data);
   p.k = static_cast<const uint8_t*>(key->data);

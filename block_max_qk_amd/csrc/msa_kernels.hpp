@@ -13,11 +13,12 @@
 //   each of the four waves streams whole blocks straight from HBM into MFMA
 //   operand registers (16x16 tiles, key tokens on M, rows on N) and many
 //   waves per CU keep enough bytes in flight.
-// prefill_kernel -- 256 rows per tile (32 tokens x 8 heads for g = 8).  A key
-//   block is loaded once per workgroup with coalesced 16-byte loads, written
-//   to LDS in a bank-conflict-free XOR-swizzled layout (int8 is converted to
-//   fp16 on the way), and read by all four waves, each holding 64 query rows
-//   in registers (32x32 MFMA tiles, key tokens on M).
+// prefill_kernel -- 384 rows per tile for 16-bit keys (48 tokens x 8 heads for
+//   g = 8), 256 for fp8 and int8.  A key block is staged once per workgroup
+//   into LDS in a bank-conflict-free XOR-swizzled layout (straight from
+//   HBM/L2 for 16-bit and fp8, widened to fp16 through registers for int8)
+//   and read by all four waves, each holding 96 (or 64) query rows in
+//   registers (32x32 MFMA tiles, key tokens on M).
 //
 // In both, a lane's accumulators hold several key tokens of one row, so the
 // 128-wide block maximum is an in-register max over the lane's values (after
@@ -32,8 +33,15 @@
 namespace msa {
 
 constexpr int kDecodeRows = 16;
-constexpr int kPrefillRows = 256;
+constexpr int kPrefillRows = 256;   // family choice threshold: half of this per request
 constexpr int kPrefillChunk = 16;   // blocks per prefill work item (fp8: twice that)
+
+// 32-row MFMA N tiles each prefill wave holds; a workgroup's tile is four
+// waves of them.  More N tiles let one key fragment read from LDS feed more
+// MFMAs, at the cost of query registers (and so waves per SIMD): 16-bit keys
+// take three (two waves per SIMD), fp8 and int8 two.
+constexpr int prefill_ntw(int kk) { return (kk == KF16 || kk == KBF16) ? 3 : 2; }
+constexpr int prefill_rows(int kk) { return 4 * 32 * prefill_ntw(kk); }
 
 // ---------------------------------------------------------------------------
 // decode
@@ -186,6 +194,9 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
 template <int KK>
 __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
   using Kd = Kind<KK>;
+  // int8: each wave's current block of column scales, staged so that every
+  // lane can read the four consecutive scales of its accumulator tokens
+  __shared__ __attribute__((aligned(16))) float dscl[Kd::is_i8 ? 4 : 1][kP];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
@@ -269,39 +280,58 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
     }
 
     const int beta = c.beta;
-    int64_t boff;
+    int64_t boff, soff;         // key byte offset, int8 scale element offset
     if (p.paged) {
-      // the page was fetched during the previous block when it was known
-      if (next_page < 0) next_page = p.block_table[(int64_t)w.b * p.MB + beta];
+      // The page was fetched during the previous block when it was known.
+      // Otherwise it is read here and made wave-uniform inside the branch,
+      // so that only this rare path waits on memory: a wait after the
+      // branch would also wait for the previous block's result store.
+      if (next_page < 0)
+        next_page = __builtin_amdgcn_readfirstlane(p.block_table[(int64_t)w.b * p.MB + beta]);
       boff = (int64_t)next_page * p.k_page_stride;
+      soff = (int64_t)next_page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
     } else {
       boff = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
+      soff = (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
     }
     next_page = -1;
     const uint8_t* kb = p.k + boff + (int64_t)hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
     const bool full = beta * kP + kP - 1 <= lim_lo;
-    const float* sb = nullptr;
-    if constexpr (Kd::is_i8) sb = p.scale + scale_offset(p, w, beta, hk);
+    // int8: the block's scales, two per lane, issued with the key loads;
+    // tokens past kv_len repeat the last valid one's (always in bounds)
+    float s_lo = 0.f, s_hi = 0.f;
+    if constexpr (Kd::is_i8) {
+      const float* sb = p.scale + soff;
+      s_lo = sb[(int64_t)min(2 * l, nvalid - 1) * p.s_row_stride];
+      s_hi = sb[(int64_t)min(2 * l + 1, nvalid - 1) * p.s_row_stride];
+    }
 
     float m = -__builtin_inff();
     if constexpr (Kd::is_f8 || Kd::is_i8) {
-      // one byte per element: a lane reads 32 contiguous bytes of its token
+      // one byte per element: a lane reads 32 contiguous bytes of its token.
+      // Token rows past kv_len re-read the last valid row (in bounds, and the
+      // mask discards them), so that every load is unconditional and all of
+      // a block's loads are in flight together.
       i32x4 kv[8][2];
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
-        const int jj = jt * 16 + n;
-        if (jj < nvalid) {
-          const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride + 32 * G;
-          kv[jt][0] = ld16_stream(kr);
-          kv[jt][1] = ld16_stream(kr + 16);
-        } else {
-          kv[jt][0] = kv[jt][1] = i32x4{0, 0, 0, 0};
-        }
+        const int jj = min(jt * 16 + n, nvalid - 1);
+        const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride + 32 * G;
+        kv[jt][0] = ld16_stream(kr);
+        kv[jt][1] = ld16_stream(kr + 16);
       }
       // next block's page index, if it belongs to the same tile
       if (p.paged && beta + 4 < c.nvis && task + 4 < s1)
         next_page = p.block_table[(int64_t)w.b * p.MB + beta + 4];
+      if constexpr (Kd::is_i8) {
+        // LDS operations of one wave complete in order, so the reads below
+        // see this store; the previous block's reads were issued before it
+        *reinterpret_cast<float2*>(&dscl[wave][2 * l]) = float2{s_lo, s_hi};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -317,16 +347,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
           acc = mfma16x16x32<KF16>(a3, qv[3], acc);
         }
         f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (Kd::is_i8) {
-          const int jr0 = jt * 16 + 4 * G;
-          if (p.s_row_stride == 1 && jr0 + 3 < nvalid) {
-            sc4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sb + jr0));
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              sc4[r] = (jr0 + r < nvalid) ? sb[(int64_t)(jr0 + r) * p.s_row_stride] : 0.f;
-          }
-        }
+        if constexpr (Kd::is_i8)
+          sc4 = *reinterpret_cast<const f32x4*>(&dscl[wave][jt * 16 + 4 * G]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int jr = jt * 16 + 4 * G + r;         // key token of acc[r]
@@ -337,18 +359,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
         }
       }
     } else {
+      // token rows past kv_len re-read the last valid row, as above
       i32x4 kv[8][4];
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
-        const int jj = jt * 16 + n;
-        if (jj < nvalid) {
-          const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride;
+        const int jj = min(jt * 16 + n, nvalid - 1);
+        const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) kv[jt][s] = ld16_stream(kr + 16 * (4 * s + G));
-        } else {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) kv[jt][s] = i32x4{0, 0, 0, 0};
-        }
+        for (int s = 0; s < 4; ++s) kv[jt][s] = ld16_stream(kr + 16 * (4 * s + G));
       }
       // next block's page index, if it belongs to the same tile
       if (p.paged && beta + 4 < c.nvis && task + 4 < s1)
@@ -386,8 +404,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
 // ---------------------------------------------------------------------------
 
 template <int KK>
-__global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(Params p) {
+__global__ __launch_bounds__(256, (Kind<KK>::is_i8 || prefill_ntw(KK) >= 3) ? 2 : 3)
+void prefill_kernel(Params p) {
   using Kd = Kind<KK>;
+  constexpr int NTW = prefill_ntw(KK);
   // Key blocks pass through an LDS ring of stages.  16-bit keys: stages of 64
   // tokens (16 KB), three deep, so a stage's copy has two compute periods to
   // land; fp8: whole 128-token blocks (16 KB), two deep; int8 (widened to
@@ -420,11 +440,11 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
   const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
   const bool busy = w.c0 < vend;      // some block of this work item is visible
 
-  int lim[2];
-  i32x4 qv[2][8];
+  int lim[NTW];
+  i32x4 qv[NTW][8];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = wave * 64 + nt * 32 + n;
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int r = wave * 32 * NTW + nt * 32 + n;
     const int ti = r / p.hpt;
     const int hg = w.hc * p.hpt + (r - ti * p.hpt);
     const bool ok = (r < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
@@ -522,15 +542,21 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
     if (tid < kP) scl[slot][tid] = sv;
   };
 
-  // The output row this lane writes: after the cross-half reduction, lanes of
-  // k group 0 hold N tile 0's rows and group 1 N tile 1's.  Each block's
-  // result is stored as soon as it is known (the L2 merges a row's columns).
-  const int orow = wave * 64 + G * 32 + n;
-  const int oti = orow / p.hpt;
-  const int ohg = w.hc * p.hpt + (orow - oti * p.hpt);
-  const bool orow_ok = orow < p.hpt * p.tpt && oti < w.ntok && ohg < p.g;
-  float* const orow_ptr =
-      p.out + (((int64_t)w.hk * p.g + ohg) * p.T + (w.t0 + oti)) * p.W;
+  // The output rows this lane writes: after the cross-half reduction both k
+  // groups hold every N tile's results; lanes of group G write N tiles G,
+  // G + 2, ...  Each block's result is stored soon after it is known (the L2
+  // merges a row's columns).
+  constexpr int NOUT = (NTW + 1) / 2;
+  bool orow_ok[NOUT];
+  float* orow_ptr[NOUT];
+#pragma unroll
+  for (int u = 0; u < NOUT; ++u) {
+    const int orow = wave * 32 * NTW + (G + 2 * u) * 32 + n;
+    const int oti = orow / p.hpt;
+    const int ohg = w.hc * p.hpt + (orow - oti * p.hpt);
+    orow_ok[u] = G + 2 * u < NTW && orow < p.hpt * p.tpt && oti < w.ntok && ohg < p.g;
+    orow_ptr[u] = p.out + (((int64_t)w.hk * p.g + ohg) * p.T + (w.t0 + oti)) * p.W;
+  }
   const int ostart = p.start_loc[w.b];
 
   const int nst = busy ? (vend - w.c0) * SPB : 0;   // stages of this work item
@@ -546,26 +572,35 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
       lstore_i8(0);
     }
   }
-  float run0 = -__builtin_inff(), run1 = -__builtin_inff();
+  // running block maxima, one per N tile; a vector value rather than an
+  // array, so that picking a lane's output tile cannot become a private
+  // memory access (which the ring's memory-counter waits would wait on)
+  static_assert(NTW <= 4, "running maxima are held in a four-wide vector");
+  f32x4 run;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
   // Block results of this lane's row collect in registers, RG blocks at a
   // time, and are written as RG consecutive floats (16-byte stores).  16-bit
   // keys run at the register limit and flush every 4 blocks; fp8 and int8
   // once per work item.
   constexpr int RG = (ASYNC && RB == 256) ? 4 : 16;
-  float resv[RG];
+  float resv[NOUT][RG];
   int pend = -1;                 // first block of a group waiting to be written
   auto flush = [&](int g0) {
-    if (orow_ok) {
 #pragma unroll
-      for (int c = 0; c < RG; c += 4) {
-        if (g0 + c < w.c1) {
-          f32x4 v;
+    for (int u = 0; u < NOUT; ++u) {
+      if (orow_ok[u]) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int beta = g0 + c + e;
-            v[e] = finish(p, w.L, ostart, beta, beta < vend, resv[c + e]);
+        for (int c = 0; c < RG; c += 4) {
+          if (g0 + c < w.c1) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int beta = g0 + c + e;
+              v[e] = finish(p, w.L, ostart, beta, beta < vend, resv[u][c + e]);
+            }
+            *reinterpret_cast<f32x4*>(orow_ptr[u] + g0 + c) = v;
           }
-          *reinterpret_cast<f32x4*>(orow_ptr + g0 + c) = v;
         }
       }
     }
@@ -597,8 +632,8 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
     }
     const uint8_t* kc = kl + slot * SBYTES;
     if (off == 0) {
-      run0 = -__builtin_inff();
-      run1 = -__builtin_inff();
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
     }
     // One pass over the block's four 32-token M tiles; MASKED selects -inf for
     // key tokens past each row's last visible one (only blocks cut by the
@@ -612,7 +647,7 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
       // LEAD + 1 fragments live.
       constexpr int PER_MT = Kd::is_f8 ? 4 : 8; // fragments per M tile
       constexpr int NFR = (ST / 32) * PER_MT;
-      constexpr int LEAD = Kd::is_f8 ? 4 : 2;
+      constexpr int LEAD = Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
       auto frag = [&](int i) -> i32x4 {
         const int mt = i / PER_MT, q = i % PER_MT;
         const int jj = mt * 32 + n;
@@ -628,44 +663,45 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
       i32x4 f[NFR];
 #pragma unroll
       for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
-      f32x16 acc0 = {}, acc1 = {};
+      f32x16 acc[NTW];
 #pragma unroll
       for (int i = 0; i < NFR; ++i) {
         if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
         const int mt = i / PER_MT, q = i % PER_MT;
         if (q == 0) {
-          acc0 = f32x16{};
-          acc1 = f32x16{};
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x16{};
         }
         if constexpr (Kd::is_f8) {
           if (q & 1) {
             const int s = q >> 1;
             const i32x8 a = cat(f[i - 1], f[i]);
-            acc0 = mfma32x32x64_f8<KK>(a, cat(qv[0][2 * s], qv[0][2 * s + 1]), acc0);
-            acc1 = mfma32x32x64_f8<KK>(a, cat(qv[1][2 * s], qv[1][2 * s + 1]), acc1);
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+              acc[nt] = mfma32x32x64_f8<KK>(a, cat(qv[nt][2 * s], qv[nt][2 * s + 1]), acc[nt]);
           }
         } else {
-          acc0 = mfma32x32x16<Kd::mfma_kind>(f[i], qv[0][q], acc0);
-          acc1 = mfma32x32x16<Kd::mfma_kind>(f[i], qv[1][q], acc1);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            acc[nt] = mfma32x32x16<Kd::mfma_kind>(f[i], qv[nt][q], acc[nt]);
         }
         if (q == PER_MT - 1) {
-          // acc[r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
+          // acc[nt][r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int jr = off + mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
-            float v0 = acc0[r], v1 = acc1[r];
-            if constexpr (Kd::is_i8) {
-              const float sc = scl[slot][jr];
-              v0 *= sc;
-              v1 *= sc;
+            float sc = 1.f;
+            if constexpr (Kd::is_i8) sc = scl[slot][jr];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+              float v = acc[nt][r];
+              if constexpr (Kd::is_i8) v *= sc;
+              if constexpr (MASKED) {
+                const int j = beta * kP + jr;
+                v = (j <= lim[nt]) ? v : -__builtin_inff();
+              }
+              run[nt] = fmaxf(run[nt], v);
             }
-            if constexpr (MASKED) {
-              const int j = beta * kP + jr;
-              v0 = (j <= lim[0]) ? v0 : -__builtin_inff();
-              v1 = (j <= lim[1]) ? v1 : -__builtin_inff();
-            }
-            run0 = fmaxf(run0, v0);
-            run1 = fmaxf(run1, v1);
           }
         }
         // keep this shape: one fragment read, its MFMAs, (an epilogue); the
@@ -680,12 +716,15 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
 
     if (off + ST == kP) {
       // the two k groups hold the two halves of each 32-token M tile
-      run0 = fmaxf(run0, __shfl_xor(run0, 32, 64));
-      run1 = fmaxf(run1, __shfl_xor(run1, 32, 64));
-      const float v = G ? run1 : run0;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) run[nt] = fmaxf(run[nt], __shfl_xor(run[nt], 32, 64));
       const int kk = (beta - w.c0) % RG;
 #pragma unroll
-      for (int k = 0; k < RG; ++k) resv[k] = (k == kk) ? v : resv[k];
+      for (int u = 0; u < NOUT; ++u) {
+        const float v = (G && 2 * u + 1 < NTW) ? run[2 * u + 1] : run[2 * u];
+#pragma unroll
+        for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+      }
       if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
     }
     if constexpr (!ASYNC) {
@@ -695,13 +734,16 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 2 : 3) void prefill_kernel(P
 
   if (pend >= 0) flush(pend);
   // columns of the work item past the last group: -inf and local_mask
-  if (orow_ok) {
-    const int done = busy ? w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG : w.c0;
-    for (int beta = done; beta < w.c1; beta += 4) {
-      f32x4 v;
+  const int done = busy ? w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG : w.c0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, ostart, beta + e, false, 0.f);
-      *reinterpret_cast<f32x4*>(orow_ptr + beta) = v;
+  for (int u = 0; u < NOUT; ++u) {
+    if (orow_ok[u]) {
+      for (int beta = done; beta < w.c1; beta += 4) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, ostart, beta + e, false, 0.f);
+        *reinterpret_cast<f32x4*>(orow_ptr[u] + beta) = v;
+      }
     }
   }
 }
