@@ -87,6 +87,15 @@ __device__ __forceinline__ i32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
 }
 
+// Keeps this wave's LDS stores ahead of its following LDS loads in the
+// instruction stream; the LDS executes one wave's operations in order, so the
+// loads then see the stores of every lane of the wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // Work decomposition.
 //

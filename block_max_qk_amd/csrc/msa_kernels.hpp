@@ -197,6 +197,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
   // int8: each wave's current block of column scales, staged so that every
   // lane can read the four consecutive scales of its accumulator tokens
   __shared__ __attribute__((aligned(16))) float dscl[Kd::is_i8 ? 4 : 1][kP];
+  // two transpose areas per wave, each one 16-token sub-tile of key rows
+  constexpr int RBY = kD * Kd::k_bytes;        // key row bytes
+  __shared__ __attribute__((aligned(16))) uint8_t dkt[4][2][16 * RBY];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
@@ -243,7 +246,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
   int cur_b = -1, cur_j = -1;
   Work w;
   i32x4 qv[4];
-  int lim = -1, lim_lo = -1, start = 0, next_page = -1;
+  int lim = -1, lim_lo = -1, start = 0;
+  // Paged keys: page indices of this wave's next blocks of the tile, lane k
+  // holding the k-th (blocks beta, beta + 4, ...), read with readlane; pk is
+  // the next lane to read (64: load again).  One load per tile instead of one
+  // per block keeps conditional memory reads out of the steady-state loop.
+  int pidx = 0, pk = 64;
+  // A block's result is stored once the next block's key loads are issued:
+  // storing it at the end of its own iteration made the compiler wait for
+  // that store (the memory counter is in order) before the next key loads.
+  bool pend_ok = false;
+  float* pend_ptr = p.out;
+  float pend_val = 0.f;
   bool row_ok = false;
   int ti = 0, hg = 0;
   for (;;) {
@@ -251,6 +265,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
       // new tile: its query rows, windows and local_mask anchor
       cur_b = c.b;
       cur_j = c.j;
+      pk = 64;
       w = tile_work(p, c, hk, hc);
       const int i0 = c.j * p.tpt;
       ti = n / p.hpt;
@@ -282,19 +297,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
     const int beta = c.beta;
     int64_t boff, soff;         // key byte offset, int8 scale element offset
     if (p.paged) {
-      // The page was fetched during the previous block when it was known.
-      // Otherwise it is read here and made wave-uniform inside the branch,
-      // so that only this rare path waits on memory: a wait after the
-      // branch would also wait for the previous block's result store.
-      if (next_page < 0)
-        next_page = __builtin_amdgcn_readfirstlane(p.block_table[(int64_t)w.b * p.MB + beta]);
-      boff = (int64_t)next_page * p.k_page_stride;
-      soff = (int64_t)next_page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
+      if (pk == 64) {
+        const int bb = beta + 4 * l;
+        pidx = bb < c.nvis ? p.block_table[(int64_t)w.b * p.MB + bb] : 0;
+        pk = 0;
+      }
+      const int page = __builtin_amdgcn_readlane(pidx, pk);
+      ++pk;
+      boff = (int64_t)page * p.k_page_stride;
+      soff = (int64_t)page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
     } else {
       boff = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
       soff = (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
     }
-    next_page = -1;
     const uint8_t* kb = p.k + boff + (int64_t)hk * p.k_head_stride;
     const int nvalid = min(kP, w.L - beta * kP);
     const bool full = beta * kP + kP - 1 <= lim_lo;
@@ -307,96 +322,127 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
       s_hi = sb[(int64_t)min(2 * l + 1, nvalid - 1) * p.s_row_stride];
     }
 
-    float m = -__builtin_inff();
+    float m;
     if constexpr (Kd::is_f8 || Kd::is_i8) {
-      // one byte per element: a lane reads 32 contiguous bytes of its token.
-      // Token rows past kv_len re-read the last valid row (in bounds, and the
-      // mask discards them), so that every load is unconditional and all of
-      // a block's loads are in flight together.
-      i32x4 kv[8][2];
+      // Key loads: instruction i reads rows 8i..8i+7 of the block whole (lane
+      // l: row 8i + l/8, 16-byte chunk l%8), eight full 128-byte lines per
+      // instruction.  (Loading straight into the MFMA operand layout would
+      // touch sixteen half lines per instruction, which measured 16% slower
+      // on random pages.)  Token rows past kv_len re-read the last valid row
+      // (in bounds; the mask discards them), so every load is unconditional
+      // and all of a block's loads are in flight together.
+      i32x4 raw[16];
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        const int jj = min(jt * 16 + n, nvalid - 1);
-        const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride + 32 * G;
-        kv[jt][0] = ld16_stream(kr);
-        kv[jt][1] = ld16_stream(kr + 16);
+      for (int i = 0; i < 16; ++i) {
+        const int row = min(8 * i + (l >> 3), nvalid - 1);
+        raw[i] = ld16_stream(kb + (int64_t)row * p.k_row_stride + 16 * (l & 7));
       }
-      // next block's page index, if it belongs to the same tile
-      if (p.paged && beta + 4 < c.nvis && task + 4 < s1)
-        next_page = p.block_table[(int64_t)w.b * p.MB + beta + 4];
       if constexpr (Kd::is_i8) {
-        // LDS operations of one wave complete in order, so the reads below
-        // see this store; the previous block's reads were issued before it
         *reinterpret_cast<float2*>(&dscl[wave][2 * l]) = float2{s_lo, s_hi};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
       }
+      // MASKED selects -inf for key tokens past the row's last visible one;
+      // only blocks cut by the window or by kv_len take it (uniform branch)
+      auto score = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        float mm = -__builtin_inff();
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (Kd::is_f8) {
-          acc = mfma16x16x128_f8<KK>(cat(kv[jt][0], kv[jt][1]), cat(qv[0], qv[1]), acc);
-        } else {
-          i32x4 a0, a1, a2, a3;
-          i8x16_to_f16x16(kv[jt][0], a0, a1);
-          i8x16_to_f16x16(kv[jt][1], a2, a3);
-          acc = mfma16x16x32<KF16>(a0, qv[0], acc);
-          acc = mfma16x16x32<KF16>(a1, qv[1], acc);
-          acc = mfma16x16x32<KF16>(a2, qv[2], acc);
-          acc = mfma16x16x32<KF16>(a3, qv[3], acc);
-        }
-        f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (Kd::is_i8)
-          sc4 = *reinterpret_cast<const f32x4*>(&dscl[wave][jt * 16 + 4 * G]);
+        for (int jt = 0; jt < 8; ++jt) {
+          // sub-tile jt (tokens 16jt..16jt+15) through the LDS: written as
+          // loaded, read back as lane (n, G) <- bytes [32G, 32G+32) of token
+          // n; 16-byte chunk c of row r sits at chunk c ^ (r & 7)
+          uint8_t* area = dkt[wave][jt & 1];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jr = jt * 16 + 4 * G + r;         // key token of acc[r]
-          float v = acc[r];
-          if constexpr (Kd::is_i8) v *= sc4[r];
-          if (!full) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
-          m = fmaxf(m, v);
+          for (int q = 0; q < 2; ++q) {
+            const int r = 8 * q + (l >> 3);
+            *reinterpret_cast<i32x4*>(area + r * 128 + (((l & 7) ^ (r & 7)) << 4)) = raw[2 * jt + q];
+          }
+          wave_lds_sync();
+          i32x4 k0 = *reinterpret_cast<const i32x4*>(area + n * 128 + (((2 * G) ^ (n & 7)) << 4));
+          i32x4 k1 = *reinterpret_cast<const i32x4*>(area + n * 128 + (((2 * G + 1) ^ (n & 7)) << 4));
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (Kd::is_f8) {
+            acc = mfma16x16x128_f8<KK>(cat(k0, k1), cat(qv[0], qv[1]), acc);
+          } else {
+            i32x4 a0, a1, a2, a3;
+            i8x16_to_f16x16(k0, a0, a1);
+            i8x16_to_f16x16(k1, a2, a3);
+            acc = mfma16x16x32<KF16>(a0, qv[0], acc);
+            acc = mfma16x16x32<KF16>(a1, qv[1], acc);
+            acc = mfma16x16x32<KF16>(a2, qv[2], acc);
+            acc = mfma16x16x32<KF16>(a3, qv[3], acc);
+          }
+          f32x4 sc4 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (Kd::is_i8)
+            sc4 = *reinterpret_cast<const f32x4*>(&dscl[wave][jt * 16 + 4 * G]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jr = jt * 16 + 4 * G + r;         // key token of acc[r]
+            float v = acc[r];
+            if constexpr (Kd::is_i8) v *= sc4[r];
+            if constexpr (MASKED) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
+            mm = fmaxf(mm, v);
+          }
         }
-      }
+        return mm;
+      };
+      if (pend_ok) *pend_ptr = pend_val;
+      m = full ? score(std::false_type{}) : score(std::true_type{});
     } else {
-      // token rows past kv_len re-read the last valid row, as above
-      i32x4 kv[8][4];
+      // instruction i reads rows 4i..4i+3 whole (lane l: row 4i + l/16,
+      // 16-byte chunk l%16): eight full lines, as above
+      i32x4 raw[32];
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        const int jj = min(jt * 16 + n, nvalid - 1);
-        const uint8_t* kr = kb + (int64_t)jj * p.k_row_stride;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kv[jt][s] = ld16_stream(kr + 16 * (4 * s + G));
+      for (int i = 0; i < 32; ++i) {
+        const int row = min(4 * i + (l >> 4), nvalid - 1);
+        raw[i] = ld16_stream(kb + (int64_t)row * p.k_row_stride + 16 * (l & 15));
       }
-      // next block's page index, if it belongs to the same tile
-      if (p.paged && beta + 4 < c.nvis && task + 4 < s1)
-        next_page = p.block_table[(int64_t)w.b * p.MB + beta + 4];
+      auto score = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        float mm = -__builtin_inff();
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int jt = 0; jt < 8; ++jt) {
+          // sub-tile jt through the LDS, read back as lane (n, G) <- chunk
+          // 4s + G of token n for k step s; chunk c of row r sits at c ^ r
+          uint8_t* area = dkt[wave][jt & 1];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma16x16x32<KK>(kv[jt][s], qv[s], acc);
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * q + (l >> 4);
+            *reinterpret_cast<i32x4*>(area + r * 256 + (((l & 15) ^ r) << 4)) = raw[4 * jt + q];
+          }
+          wave_lds_sync();
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jr = jt * 16 + 4 * G + r;
-          float v = acc[r];
-          if (!full) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
-          m = fmaxf(m, v);
+          for (int s = 0; s < 4; ++s) {
+            const i32x4 kf =
+                *reinterpret_cast<const i32x4*>(area + n * 256 + (((4 * s + G) ^ n) << 4));
+            acc = mfma16x16x32<KK>(kf, qv[s], acc);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jr = jt * 16 + 4 * G + r;
+            float v = acc[r];
+            if constexpr (MASKED) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
+            mm = fmaxf(mm, v);
+          }
         }
-      }
+        return mm;
+      };
+      if (pend_ok) *pend_ptr = pend_val;
+      m = full ? score(std::false_type{}) : score(std::true_type{});
     }
     // the four k groups hold disjoint key tokens of the same row
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (G == 0 && row_ok) {
-      const int64_t h = (int64_t)hk * p.g + hg;
-      p.out[(h * p.T + (w.t0 + ti)) * p.W + beta] = finish(p, w.L, start, beta, true, m);
-    }
+    pend_ok = G == 0 && row_ok;
+    pend_ptr = p.out + (((int64_t)hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W + beta;
+    pend_val = finish(p, w.L, start, beta, true, m);
 
     task += 4;
     if (task >= s1) break;
     advance(p, c, 4);
   }
+  if (pend_ok) *pend_ptr = pend_val;
 }
 
 // ---------------------------------------------------------------------------
