@@ -87,6 +87,13 @@ __device__ __forceinline__ i32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
 }
 
+// A value every lane of the wave holds, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Keeps this wave's LDS stores ahead of its following LDS loads in the
 // instruction stream; the LDS executes one wave's operations in order, so the
 // loads then see the stores of every lane of the wave.

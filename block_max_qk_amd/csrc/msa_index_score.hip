@@ -180,7 +180,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
 
   // sizes the kernels index with 32-bit integers
   if (W > (1 << 24) || Hq > (1 << 16) || batch > (1 << 30) || T > (int64_t(1) << 31) - 1 ||
-      s_row * kb > INT32_MAX || s_head * kb > INT32_MAX)
+      (msa::kP - 1) * s_row * kb + msa::kD * kb > INT32_MAX || s_head * kb > INT32_MAX)
     return MSA_ERR_SHAPE;
 
   if (!aligned16(query->data) || !aligned16(key->data) || !aligned16(out))

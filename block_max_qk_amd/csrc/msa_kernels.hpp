@@ -310,7 +310,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
       boff = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
       soff = (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
     }
-    const uint8_t* kb = p.k + boff + (int64_t)hk * p.k_head_stride;
+    // wave-uniform block base (scalar registers); per-lane offsets within a
+    // block fit 32 bits (checked on the host), which gives the loads the
+    // scalar-base + 32-bit-offset form
+    const uint8_t* kb = p.k + uniform64(boff + (int64_t)hk * p.k_head_stride);
     const int nvalid = min(kP, w.L - beta * kP);
     const bool full = beta * kP + kP - 1 <= lim_lo;
     // int8: the block's scales, two per lane, issued with the key loads;
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = min(8 * i + (l >> 3), nvalid - 1);
-        raw[i] = ld16_stream(kb + (int64_t)row * p.k_row_stride + 16 * (l & 7));
+        raw[i] = ld16_stream(kb + (uint32_t)(row * p.k_row_stride + 16 * (l & 7)));
       }
       if constexpr (Kd::is_i8) {
         *reinterpret_cast<float2*>(&dscl[wave][2 * l]) = float2{s_lo, s_hi};
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int row = min(4 * i + (l >> 4), nvalid - 1);
-        raw[i] = ld16_stream(kb + (int64_t)row * p.k_row_stride + 16 * (l & 15));
+        raw[i] = ld16_stream(kb + (uint32_t)(row * p.k_row_stride + 16 * (l & 15)));
       }
       auto score = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;

@@ -121,7 +121,9 @@ typedef struct {
  * memory and keeps no state between calls.  Returns MSA_OK or an error
  * status; T = 0 returns MSA_OK without launching anything.  query, key and
  * out must be 16-byte aligned and a paged key's dim0 stride a multiple of 16
- * bytes (MSA_ERR_STRIDE otherwise).
+ * bytes (MSA_ERR_STRIDE otherwise).  Sizes past the kernels' 32-bit indexing
+ * return MSA_ERR_SHAPE: out_width > 2^24, Hq > 2^16, batch > 2^30, T >= 2^31,
+ * or one 128-token block of one head spanning 2 GiB or more of key memory.
  */
 msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
                              const int32_t* start_loc, const int32_t* block_table,
