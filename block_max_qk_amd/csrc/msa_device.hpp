@@ -87,6 +87,16 @@ __device__ __forceinline__ i32x4 ld16_stream(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
 }
 
+// A loaded value, waited for here.  Used on rare paths inside the decode
+// loop (new tile, new request): without it the compiler may place the wait
+// for such a load after the branch, on every iteration, where (the memory
+// counter being in order) it would also wait for the previous block's result
+// store.
+__device__ __forceinline__ int consumed(int v) {
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(v));
+  return v;
+}
+
 // A value every lane of the wave holds, moved to scalar registers.
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);

@@ -80,7 +80,7 @@ struct Cursor {
 // Per-lane view of 64 consecutive requests: lengths, their work-list and
 // tile counts, and wave-wide inclusive prefix sums of those.
 struct Scan64 {
-  int lq, kv, tasks, tiles;
+  int cu, lq, kv, tasks, tiles;
   int inc_tasks, inc_tiles;
   int64_t inc_kv;
 };
@@ -88,9 +88,10 @@ struct Scan64 {
 __device__ __forceinline__ Scan64 scan64(const Params& p, int base) {
   Scan64 s;
   const int b = base + lane_id();
-  s.lq = s.kv = s.tasks = s.tiles = 0;
+  s.cu = s.lq = s.kv = s.tasks = s.tiles = 0;
   if (b < p.B) {
-    s.lq = p.cu_q[b + 1] - p.cu_q[b];
+    s.cu = p.cu_q[b];
+    s.lq = p.cu_q[b + 1] - s.cu;
     s.kv = p.kv_len[b];
     s.tiles = tiles_of(p, s.lq);
     for (int j = 0; j < s.tiles; ++j) s.tasks += tile_blocks(p, s.kv, s.lq, j);
@@ -131,7 +132,7 @@ __device__ __forceinline__ void seek(const Params& p, const Scan64& first, int t
       c.Lq = __shfl(s.lq, src, 64);
       c.L = __shfl(s.kv, src, 64);
       c.koff = kacc + __shfl(s.inc_kv, src, 64) - c.L;
-      c.cu = p.cu_q[c.b];
+      c.cu = __shfl(s.cu, src, 64);
       int local = tau - (acc + __shfl(incl, src, 64) - __shfl(cnt, src, 64));
       if (by_tile) {
         c.j = local;
@@ -167,7 +168,7 @@ __device__ __forceinline__ void advance(const Params& p, Cursor& c, int step) {
       ++c.b;
       c.cu = p.cu_q[c.b];
       c.Lq = p.cu_q[c.b + 1] - c.cu;
-      c.L = p.kv_len[c.b];
+      c.L = consumed(p.kv_len[c.b]);
       c.j = 0;
     }
     c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
@@ -215,31 +216,46 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
   Scan64 first;
   count_work(p, first, ntask, ntile);
 
-  // fill pass: tiles wi, wi + gu, ... get -inf (and local_mask) on the
-  // columns past their last visible block
-  for (int k = wi; k < ntile; k += gu) {
-    Cursor c;
-    seek(p, first, k, true, c);
-    const Work w = tile_work(p, c, hk, hc);
-    const int start = p.start_loc[w.b];
-    const int ncol = p.W - c.nvis;
-    for (int e = threadIdx.x; e < kDecodeRows * ncol; e += 256) {
-      const int r = e / ncol;
-      const int beta = c.nvis + (e - r * ncol);
+  // Fill pass, run after the compute pass: the columns past each tile's last
+  // visible block get -inf (and local_mask).  Items are (tile, row) pairs,
+  // dealt to the workgroups in turn; a row's columns are written as 16-byte
+  // stores (a scalar head up to the first 16-byte boundary, which the compute
+  // pass does not touch).  Run first, its stores and index reads delayed
+  // every wave's first key loads by several microseconds.
+  auto fill_pass = [&]() {
+    for (int it = wi; it < ntile * kDecodeRows; it += gu) {
+      const int k = it / kDecodeRows;
+      const int r = it - k * kDecodeRows;
+      Cursor c;
+      seek(p, first, k, true, c);
+      const Work w = tile_work(p, c, hk, hc);
       const int ri = r / p.hpt;
       const int rh = hc * p.hpt + (r - ri * p.hpt);
       if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
-      const int64_t h = (int64_t)hk * p.g + rh;
-      p.out[(h * p.T + (w.t0 + ri)) * p.W + beta] = finish(p, w.L, start, beta, false, 0.f);
+      float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
+      const int start = p.start_loc[w.b];
+      const int v0 = c.nvis;
+      const int a0 = min((v0 + 3) & ~3, p.W);
+      if ((int)threadIdx.x < a0 - v0)
+        row[v0 + threadIdx.x] = finish(p, w.L, start, v0 + threadIdx.x, false, 0.f);
+      for (int cc = a0 + 4 * (int)threadIdx.x; cc < p.W; cc += 4 * 256) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, start, cc + e, false, 0.f);
+        *reinterpret_cast<f32x4*>(row + cc) = v;
+      }
     }
-  }
+  };
 
   // compute pass over this workgroup's slice of the work list
   const int per = (ntask + gu - 1) / gu;
   const int s0 = wi * per;
   const int s1 = min(ntask, s0 + per);
   int task = s0 + wave;
-  if (task >= s1) return;
+  if (task >= s1) {
+    fill_pass();
+    return;
+  }
 
   Cursor c;
   seek(p, first, task, false, c);
@@ -299,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
     if (p.paged) {
       if (pk == 64) {
         const int bb = beta + 4 * l;
-        pidx = bb < c.nvis ? p.block_table[(int64_t)w.b * p.MB + bb] : 0;
+        pidx = consumed(bb < c.nvis ? p.block_table[(int64_t)w.b * p.MB + bb] : 0);
         pk = 0;
       }
       const int page = __builtin_amdgcn_readlane(pidx, pk);
@@ -446,6 +462,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
     advance(p, c, 4);
   }
   if (pend_ok) *pend_ptr = pend_val;
+  fill_pass();
 }
 
 // ---------------------------------------------------------------------------
