@@ -193,14 +193,14 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
 }
 
 template <int KK>
-__global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
+__global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Params p) {
   using Kd = Kind<KK>;
   // int8: each wave's current block of column scales, staged so that every
   // lane can read the four consecutive scales of its accumulator tokens
   __shared__ __attribute__((aligned(16))) float dscl[Kd::is_i8 ? 4 : 1][kP];
-  // two transpose areas per wave, each one 16-token sub-tile of key rows
+  // four transpose areas per wave, each one 16-token sub-tile of key rows
   constexpr int RBY = kD * Kd::k_bytes;        // key row bytes
-  __shared__ __attribute__((aligned(16))) uint8_t dkt[4][2][16 * RBY];
+  __shared__ __attribute__((aligned(16))) uint8_t dkt[4][4][16 * RBY];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
@@ -367,16 +367,23 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
         float mm = -__builtin_inff();
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-          // sub-tile jt (tokens 16jt..16jt+15) through the LDS: written as
-          // loaded, read back as lane (n, G) <- bytes [32G, 32G+32) of token
-          // n; 16-byte chunk c of row r sits at chunk c ^ (r & 7)
-          uint8_t* area = dkt[wave][jt & 1];
+          // sub-tiles pass through the LDS four at a time (tokens 16jt..16jt+15
+          // in area jt % 4): written as loaded, read back as lane (n, G) <-
+          // bytes [32G, 32G+32) of token n; 16-byte chunk c of row r sits at
+          // chunk c ^ (r & 7)
+          uint8_t* area = dkt[wave][jt & 3];
+          if ((jt & 3) == 0) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int r = 8 * q + (l >> 3);
-            *reinterpret_cast<i32x4*>(area + r * 128 + (((l & 7) ^ (r & 7)) << 4)) = raw[2 * jt + q];
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const int r = 8 * q + (l >> 3);
+                *reinterpret_cast<i32x4*>(dkt[wave][u] + r * 128 + (((l & 7) ^ (r & 7)) << 4)) =
+                    raw[2 * (jt + u) + q];
+              }
+            }
+            wave_lds_sync();
           }
-          wave_lds_sync();
           i32x4 k0 = *reinterpret_cast<const i32x4*>(area + n * 128 + (((2 * G) ^ (n & 7)) << 4));
           i32x4 k1 = *reinterpret_cast<const i32x4*>(area + n * 128 + (((2 * G + 1) ^ (n & 7)) << 4));
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -421,15 +428,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(Params p) {
         float mm = -__builtin_inff();
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-          // sub-tile jt through the LDS, read back as lane (n, G) <- chunk
-          // 4s + G of token n for k step s; chunk c of row r sits at c ^ r
-          uint8_t* area = dkt[wave][jt & 1];
+          // sub-tiles pass through the LDS four at a time, read back as lane
+          // (n, G) <- chunk 4s + G of token n for k step s; chunk c of row r
+          // sits at c ^ r
+          uint8_t* area = dkt[wave][jt & 3];
+          if ((jt & 3) == 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = 4 * q + (l >> 4);
-            *reinterpret_cast<i32x4*>(area + r * 256 + (((l & 15) ^ r) << 4)) = raw[4 * jt + q];
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int r = 4 * q + (l >> 4);
+                *reinterpret_cast<i32x4*>(dkt[wave][u] + r * 256 + (((l & 15) ^ r) << 4)) =
+                    raw[4 * (jt + u) + q];
+              }
+            }
+            wave_lds_sync();
           }
-          wave_lds_sync();
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
