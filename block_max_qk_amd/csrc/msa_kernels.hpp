@@ -577,24 +577,28 @@ void prefill_kernel(Params p) {
   // always exactly NI copy instructions per wave (the ring's waits count
   // them): token rows at or past kv_len copy row 0 of the block instead, which
   // the masked path discards
-  auto stage_async = [&](int sg, int slot, int64_t kbytes) {
+  // copy instruction q of stage sg
+  auto stage_copy = [&](int q, int sg, int slot, int64_t kbytes) {
     const int beta = w.c0 + sg / SPB;
     const int off = (sg % SPB) * ST;
-    const uint8_t* kb = p.k + kbytes + (int64_t)w.hk * p.k_head_stride;
+    // wave-uniform block base; offsets within a block fit 32 bits (checked on
+    // the host)
+    const uint8_t* kb = p.k + uniform64(kbytes + (int64_t)w.hk * p.k_head_stride);
     const int nvalid = min(kP, w.L - beta * kP);
     constexpr int RPI = 1024 / RB;                  // tokens per copy instruction
+    const int X = wave * NI + q;
+    const int jl = X * RPI + l / (RB / 16);         // token within the stage
+    const int pos = l % (RB / 16);
+    const int c = pos ^ (RB == 256 ? (jl & 15) : ((jl >> 1) & 7));
+    const int jj = off + jl;
+    const int src = jj < nvalid ? jj : 0;
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>(kb + (uint32_t)(src * p.k_row_stride + 16 * c)),
+        (__attribute__((address_space(3))) void*)(kl + slot * SBYTES + X * 1024), 16, 0, 0);
+  };
+  auto stage_async = [&](int sg, int slot, int64_t kbytes) {
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int X = wave * NI + q;
-      const int jl = X * RPI + l / (RB / 16);       // token within the stage
-      const int pos = l % (RB / 16);
-      const int c = pos ^ (RB == 256 ? (jl & 15) : ((jl >> 1) & 7));
-      const int jj = off + jl;
-      const int src = jj < nvalid ? jj : 0;
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(kb + (int64_t)src * p.k_row_stride + 16 * c),
-          (__attribute__((address_space(3))) void*)(kl + slot * SBYTES + X * 1024), 16, 0, 0);
-    }
+    for (int q = 0; q < NI; ++q) stage_copy(q, sg, slot, kbytes);
   };
   auto gload_i8 = [&](int beta) {
     const uint8_t* kb = p.k + block_bytes(beta) + (int64_t)w.hk * p.k_head_stride;
@@ -703,12 +707,16 @@ void prefill_kernel(Params p) {
       flush(pend);
       pend = -1;
     }
-    if (sg + RING - 1 < nst) {
-      if constexpr (ASYNC)
-        stage_async(sg + RING - 1, (sg + RING - 1) % RING,
-                    block_bytes(w.c0 + (sg + RING - 1) / SPB));
-      else
-        gload_i8(beta + 1);
+    // The copy of stage sg + RING - 1 (into the slot every wave has just
+    // left) is issued from inside this stage's compute, spread over it where
+    // registers allow: issued all at once after the barrier, the copies of a
+    // workgroup's four waves stalled instruction issue for hundreds of
+    // cycles.
+    const int csg = sg + RING - 1;
+    const bool copy_next = csg < nst;
+    const int64_t ckb = (ASYNC && copy_next) ? block_bytes(w.c0 + csg / SPB) : 0;
+    if constexpr (!ASYNC) {
+      if (copy_next) gload_i8(beta + 1);
     }
     const uint8_t* kc = kl + slot * SBYTES;
     if (off == 0) {
@@ -746,6 +754,17 @@ void prefill_kernel(Params p) {
       f32x16 acc[NTW];
 #pragma unroll
       for (int i = 0; i < NFR; ++i) {
+        if constexpr (ASYNC) {
+          // copy points per stage: two for 16-bit keys; one for fp8, whose
+          // three waves per SIMD leave no registers for more
+          constexpr int CPTS = RB == 256 ? 2 : 1;
+          static_assert(NFR % CPTS == 0 && NI % CPTS == 0, "copies spread evenly");
+          if (copy_next && i % (NFR / CPTS) == 0) {
+#pragma unroll
+            for (int q = 0; q < NI / CPTS; ++q)
+              stage_copy((i / (NFR / CPTS)) * (NI / CPTS) + q, csg, csg % RING, ckb);
+          }
+        }
         if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
         const int mt = i / PER_MT, q = i % PER_MT;
         if (q == 0) {
