@@ -12,7 +12,9 @@ conversion over all codes; a vectorised brute force (full Q.K^T -> mask ->
 reshape -> amax, the form of the DSA block-selection sketch); closed forms for
 the causal window; GQA, layout, paging, poison and homogeneity invariants; the
 int8 dequant identity; the local_mask constants; and the worked tiny example's
-structure.  Finite values of the worked example are not printed by the pages,
+structure.  The top-k selection is pinned by a rank-counting brute force, by
+its invariance under a strictly increasing map of the scores (the exp-free
+property) and by constructed cases (ties, -inf rows, forced blocks).  Finite values of the worked example are not printed by the pages,
 so beyond the brute force they are parity-unpinned.
 """
 from __future__ import annotations
@@ -88,6 +90,8 @@ def _bind(lib):
     lib.orc_out_width.restype = c.c_int64
     lib.orc_decode_buffer.argtypes = [p, c.c_int, c.c_int64, p]
     lib.orc_decode_buffer.restype = None
+    lib.orc_block_topk.argtypes = [p, c.c_int64, c.c_int64, c.c_int64, c.c_int64, c.c_int, p]
+    lib.orc_block_topk.restype = c.c_int
     return lib
 
 
@@ -202,3 +206,21 @@ def index_score_case(case, nthreads: int = 0, lib=None) -> torch.Tensor:
 
 def index_score_case_points(case, points, nthreads: int = 0, lib=None) -> torch.Tensor:
     return index_score_points(**case_args(case), points=points, nthreads=nthreads, lib=lib)
+
+
+def block_topk(scores: torch.Tensor, num_valid: Optional[int] = None, k: int = 16,
+               lib=None) -> torch.Tensor:
+    """Top-k block selection on a CPU float32 score tensor [Hq, T, W]: for each
+    (t, h) the k best blocks among beta < num_valid (default W) with a score
+    above -inf, highest score first and ties to the lower index, returned as
+    int32 [T, Hq, k] in ascending block order with -1 for missing entries."""
+    assert scores.device.type == "cpu" and scores.dtype == torch.float32 and scores.dim() == 3
+    s = scores.contiguous()
+    Hq, T, W = s.shape
+    nv = W if num_valid is None else int(num_valid)
+    out = torch.empty((T, Hq, k), dtype=torch.int32)
+    rc = (lib or load()).orc_block_topk(ctypes.c_void_p(s.data_ptr()), Hq, T, W, nv, int(k),
+                                        ctypes.c_void_p(out.data_ptr()))
+    if rc != 0:
+        raise ValueError("block_topk: contract violation (%d)" % rc)
+    return out

@@ -329,3 +329,70 @@ int orc_index_score_points(const void* q, int q_dtype, int64_t T, int Hq, int D,
   free(a.koff);
   return used;
 }
+
+/* ------------------------------------------------------------------------
+ * Top-k block selection on the score rows (the follow-on stage the pages
+ * describe after the block score: the MiniMax-M3 MSA deep-dive, section 4.7
+ * "Equation (7): Top-k Block Selection" and section 5.3 "Top-k", with the
+ * sparse_topk_select contract listed there; section 6.1 "Exp-free Top-k").
+ *
+ * For each query token t and index head h, over the row score[h, t, :]:
+ *   candidates  = blocks beta < num_valid whose score is above -inf (a block
+ *                 with no visible key is invalid; NaN is never a candidate);
+ *   order       = by score, highest first, equal scores by lower beta first
+ *                 (the pages leave the tie order open; this is the reading);
+ *   selection   = the first min(k, #candidates) of that order;
+ *   output      = out[t, h, 0:k]: the selected block indices in ascending
+ *                 index order (not score order), then -1 for the rest.
+ * Selection works on the raw scores (no exp or normalisation).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float s;
+  int64_t b;
+} orc_cand;
+
+static int orc_cand_order(const void* x, const void* y) {
+  const orc_cand* u = (const orc_cand*)x;
+  const orc_cand* v = (const orc_cand*)y;
+  if (u->s > v->s) return -1;
+  if (u->s < v->s) return 1;
+  return (u->b > v->b) - (u->b < v->b);
+}
+
+static int orc_index_order(const void* x, const void* y) {
+  const int32_t u = *(const int32_t*)x, v = *(const int32_t*)y;
+  return (u > v) - (u < v);
+}
+
+/* scores: [Hq, T, W] float32; out: [T, Hq, k] int32.  Returns 0, or -1 for a
+ * contract violation (negative sizes, num_valid outside [0, W], k outside
+ * [1, 64], W above 2^31 - 1). */
+int orc_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t W,
+                   int64_t num_valid, int k, int32_t* out) {
+  if (Hq < 0 || T < 0 || W < 0 || W > INT32_MAX || num_valid < 0 || num_valid > W ||
+      k < 1 || k > 64)
+    return -1;
+  orc_cand* cand = (orc_cand*)malloc((size_t)(W > 0 ? W : 1) * sizeof(orc_cand));
+  int32_t sel[64];
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < Hq; ++h) {
+      const float* row = scores + (h * T + t) * W;
+      int64_t n = 0;
+      for (int64_t b = 0; b < num_valid; ++b) {
+        if (row[b] > -INFINITY) {
+          cand[n].s = row[b];
+          cand[n].b = b;
+          ++n;
+        }
+      }
+      qsort(cand, (size_t)n, sizeof(orc_cand), orc_cand_order);
+      const int m = n < k ? (int)n : k;
+      for (int i = 0; i < m; ++i) sel[i] = (int32_t)cand[i].b;
+      qsort(sel, (size_t)m, sizeof(int32_t), orc_index_order);
+      int32_t* dst = out + (t * Hq + h) * k;
+      for (int i = 0; i < k; ++i) dst[i] = i < m ? sel[i] : -1;
+    }
+  }
+  free(cand);
+  return 0;
+}
