@@ -29,7 +29,7 @@ LAYOUT_CODE = {"TND": 0, "BBND": 1, "BNBD": 2}
 STATUS_NAMES = ["MSA_OK", "MSA_ERR_NULL", "MSA_ERR_LAYOUT", "MSA_ERR_DTYPE", "MSA_ERR_SHAPE",
                 "MSA_ERR_STRIDE", "MSA_ERR_SCALE", "MSA_ERR_ATTR", "MSA_ERR_HIP"]
 EXPORTED = ("msa_index_score", "msa_index_score_family", "msa_index_score_out_width",
-            "msa_status_str", "msa_index_score_kernel_family")
+            "msa_status_str", "msa_index_score_kernel_family", "msa_block_topk")
 
 
 class MsaTensor(ctypes.Structure):
@@ -78,6 +78,9 @@ def load_library(path: Optional[str] = None):
         lib.msa_index_score_kernel_family.argtypes = [ctypes.c_int64, ctypes.c_int32,
                                                       ctypes.c_int32, ctypes.c_int32]
         lib.msa_index_score_kernel_family.restype = ctypes.c_int32
+        lib.msa_block_topk.argtypes = [ptr, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int32, ptr, ptr]
+        lib.msa_block_topk.restype = ctypes.c_int
         if path is None:
             _lib = lib
         return lib
@@ -187,3 +190,37 @@ def index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Tensor,
     return msa_index_score(query, key, start_loc, block_table, scale, actual_seq_qlen,
                            actual_seq_klen, lay, sparse_mode, init_blocks, local_blocks, out,
                            max_blocks, stream=stream, family=family)
+
+
+def msa_block_topk(scores: torch.Tensor, num_valid: int, k: int, out: torch.Tensor,
+                   stream=None) -> torch.Tensor:
+    """Call the C ABI: ``out`` ([T, Hq, k] int32) receives, for every row of
+    ``scores`` ([Hq, T, W] float32 on the same device), the k best blocks
+    below ``num_valid`` in ascending block order with a -1 tail;
+    asynchronous on ``stream`` (default: torch's current stream)."""
+    lib = load_library()
+    if scores.dtype != torch.float32 or not scores.is_contiguous() or scores.dim() != 3:
+        raise ValueError("scores must be a contiguous float32 [Hq, T, W] tensor")
+    Hq, T, W = scores.shape
+    if out.dtype != torch.int32 or not out.is_contiguous() or tuple(out.shape) != (T, Hq, k):
+        raise ValueError(f"out must be a contiguous int32 [{T}, {Hq}, {k}] tensor")
+    if out.device != scores.device:
+        raise ValueError(f"scores are on {scores.device}, out on {out.device}")
+    if stream is None:
+        stream = torch.cuda.current_stream(scores.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    st = lib.msa_block_topk(_ptr(scores), Hq, T, W, int(num_valid), int(k), _ptr(out),
+                            ctypes.c_void_p(stream))
+    if st != 0:
+        raise MsaError(st, msa_status_str(st))
+    return out
+
+
+def block_topk(scores: torch.Tensor, num_valid: Optional[int] = None, k: int = 16,
+               stream=None) -> torch.Tensor:
+    """Allocate ``[T, Hq, k]`` int32 and fill it with the top-k selection of
+    the score rows (``num_valid`` defaults to the row width)."""
+    Hq, T, W = scores.shape
+    out = torch.empty((T, Hq, k), dtype=torch.int32, device=scores.device)
+    return msa_block_topk(scores, W if num_valid is None else num_valid, k, out, stream=stream)

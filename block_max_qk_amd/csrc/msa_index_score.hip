@@ -1,6 +1,7 @@
-// Host side of the msa_index_score C ABI: argument validation (all of it
-// before any HIP call), work planning, and the launch of one gfx950 kernel on
-// the caller's stream.  The library allocates nothing and keeps no state.
+// Host side of the msa_index_score C ABI (and of msa_block_topk, the top-k
+// selection over its output): argument validation (all of it before any HIP
+// call), work planning, and the launch of one gfx950 kernel on the caller's
+// stream.  The library allocates nothing and keeps no state.
 #include "msa_index_score.h"
 
 #include <hip/hip_runtime.h>
@@ -9,6 +10,7 @@
 #include <cstdint>
 
 #include "msa_kernels.hpp"
+#include "msa_topk.hpp"
 
 namespace {
 
@@ -278,6 +280,37 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int64_t out_width, void* stream, int32_t family) {
   return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
              layout, sparse_mode, init_blocks, local_blocks, out, out_width, stream, family);
+}
+
+msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
+                            int64_t num_valid, int32_t k, int32_t* out, void* stream) {
+  if (Hq < 0 || T < 0 || width < 0 || width > (1 << 24) || num_valid < 0 || num_valid > width)
+    return MSA_ERR_SHAPE;
+  if (k < 1 || k > msa::kTopkMax) return MSA_ERR_ATTR;
+  if (Hq > 0 && T > INT64_MAX / Hq) return MSA_ERR_SHAPE;
+  const int64_t rows = Hq * T;
+  if (rows == 0) return MSA_OK;
+  if (rows > (int64_t)INT32_MAX * 4) return MSA_ERR_SHAPE;
+  if (!out || (num_valid > 0 && !scores)) return MSA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return MSA_ERR_STRIDE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int nv = (int)num_valid;
+  // keys of up to 64 * J blocks stay in registers; longer rows are re-read
+  if (nv <= 128)
+    hipLaunchKernelGGL(msa::topk_kernel<2>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+  else if (nv <= 256)
+    hipLaunchKernelGGL(msa::topk_kernel<4>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+  else if (nv <= 512)
+    hipLaunchKernelGGL(msa::topk_kernel<8>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+  else if (nv <= 1024)
+    hipLaunchKernelGGL(msa::topk_kernel<16>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+  else if (nv <= 2048)
+    hipLaunchKernelGGL(msa::topk_kernel<32>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+  else
+    hipLaunchKernelGGL(msa::topk_kernel<0>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }

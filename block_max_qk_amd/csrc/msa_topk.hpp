@@ -1,0 +1,98 @@
+// Top-k block selection on the score rows, for gfx950.
+//
+// The stage after the block score (the MiniMax-M3 MSA deep-dive, section 4.7
+// "Top-k Block Selection" and section 5.3 "Top-k" with the sparse_topk_select
+// contract; section 6.1 "Exp-free Top-k"): for every (query token t, index
+// head h), the k best blocks of the row score[h, t, 0:num_valid] among those
+// scoring above -inf, highest score first and equal scores by lower block
+// index, written to out[t, h, 0:k] in ascending block order with a -1 tail.
+// It works on the raw scores (no exp or normalisation).
+//
+// One wave per row.  Scores map to order-preserving 32-bit keys (0 for blocks
+// that cannot be selected); the k-th largest key tau is found bit by bit from
+// the top, each step counting the keys at or above a candidate threshold with
+// wave ballots (the counts stay in scalar registers).  The selection is then
+// compacted in index order: every key above tau, and keys equal to tau while
+// slots remain, lowest index first -- which also yields the ascending output
+// without a sort.  Rows of up to 64 * J blocks keep their keys in registers
+// (read once, 256 contiguous bytes per load instruction); longer rows (J = 0)
+// re-read the row, from L2, at every step.
+#pragma once
+
+#include "msa_device.hpp"
+
+namespace msa {
+
+constexpr int kTopkMax = 64;   // k is at most one wave of lanes
+
+// Order-preserving key of a score that can be selected; 0 for -inf and NaN.
+__device__ __forceinline__ uint32_t topk_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return f > -__builtin_inff() ? key : 0u;
+}
+
+template <int J>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
+                                                   int64_t rows, int64_t T, int64_t Hq,
+                                                   int64_t W, int nv, int k,
+                                                   int32_t* __restrict__ out) {
+  const int l = lane_id();
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row h * T + t
+  if (r >= rows) return;
+  const float* row = scores + r * W;
+  const int64_t h = r / T;
+  const int64_t t = r - h * T;
+  int32_t* const dst = out + (t * Hq + h) * k;
+  const int nch = (nv + 63) / 64;          // 64-block chunks holding candidates
+  const int nj = J > 0 ? J : nch;
+
+  uint32_t keys[J > 0 ? J : 1];
+  if constexpr (J > 0) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int b = j * 64 + l;
+      keys[j] = b < nv ? topk_key(__builtin_nontemporal_load(row + b)) : 0u;
+    }
+  }
+  auto key = [&](int j) -> uint32_t {
+    if constexpr (J > 0) {
+      return keys[j];
+    } else {
+      const int b = j * 64 + l;
+      return b < nv ? topk_key(row[b]) : 0u;
+    }
+  };
+  // number of keys >= c over the row
+  auto count_ge = [&](uint32_t c) -> int {
+    int n = 0;
+    for (int j = 0; j < nj; ++j) n += __popcll(__ballot(key(j) >= c));
+    return n;
+  };
+
+  // tau = the k-th largest key, or 0 when the row has at most k candidates
+  uint32_t tau = 0;
+  if (count_ge(1u) > k) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = tau | (1u << bit);
+      if (count_ge(c) >= k) tau = c;
+    }
+  }
+  // keys above tau all fit; ties at tau fill the remaining slots
+  const int need_eq = tau == 0 ? 0 : k - count_ge(tau + 1u);
+  const uint64_t below = (1ull << l) - 1ull;
+  int taken = 0, eq_seen = 0;
+  for (int j = 0; j < nj; ++j) {
+    const uint32_t kv = key(j);
+    const bool eq = tau != 0u && kv == tau;
+    const uint64_t em = __ballot(eq);
+    const bool take = kv > tau || (eq && eq_seen + __popcll(em & below) < need_eq);
+    const uint64_t tm = __ballot(take);
+    if (take) dst[taken + __popcll(tm & below)] = j * 64 + l;
+    taken += __popcll(tm);
+    eq_seen += __popcll(em);
+  }
+  if (l < k && l >= taken) dst[l] = -1;
+}
+
+}  // namespace msa

@@ -146,6 +146,34 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int32_t init_blocks, int32_t local_blocks, float* out,
                                     int64_t out_width, void* stream, int32_t family);
 
+/* Top-k block selection on the score rows: the stage the pages place after
+ * the block score (the MiniMax-M3 MSA deep-dive, section 4.7 "Top-k Block
+ * Selection", section 5.3 "Top-k" with the sparse_topk_select contract,
+ * section 6.1 "Exp-free Top-k").
+ *
+ * For every query token t and index head h, among the blocks beta < num_valid
+ * of the row scores[h, t, :] whose score is above -inf (NaN never qualifies),
+ * the k with the highest scores, equal scores taken by lower block index,
+ * are written to out[t, h, 0:k] in ascending block order; the slots past the
+ * number selected hold -1.  Selection works on the raw scores.
+ *
+ * scores     device float32 [Hq, T, width], compact (msa_index_score's out),
+ *            4-byte aligned; not read when num_valid = 0.
+ * Hq, T, width  sizes, >= 0, width <= 2^24.
+ * num_valid  blocks to consider, in [0, width] (the table width MB for an
+ *            msa_index_score output; columns past it are padding).
+ * k          1..64 (the sparse_topk_select contract uses 16).
+ * out        device int32 [T, Hq, k], compact, 4-byte aligned, written in full.
+ * stream     hipStream_t (as void*); the call is asynchronous on it.
+ *
+ * Ownership: caller-owned pointers; nothing is allocated or kept.  Returns
+ * MSA_OK (also, without launching, when Hq * T = 0), MSA_ERR_SHAPE for sizes
+ * out of range, MSA_ERR_ATTR for k out of range, MSA_ERR_NULL for a NULL
+ * pointer the call must use, MSA_ERR_STRIDE for a misaligned one,
+ * MSA_ERR_HIP if the launch fails. */
+msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
+                            int64_t num_valid, int32_t k, int32_t* out, void* stream);
+
 /* Output width RoundUp(max(max_blocks, 1), 16) (guide, section 五: the last
  * axis is aligned to 16, and an all-empty packed batch clamps MB to 1). */
 int64_t msa_index_score_out_width(int64_t max_blocks);

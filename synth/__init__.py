@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the MSA index-score operator.
 
 This package only draws and lays out input tensors (queries, paged or packed
-keys, int8 scales, block tables, sequence lengths).  It holds none of the
+keys, int8 scales, block tables, sequence lengths, and score rows for the
+top-k selection).  It holds none of the
 operator's arithmetic, so both the CPU oracle's tests and the GPU path's tests
 and benchmark can use it without sharing any scoring code.
 """
@@ -14,4 +15,5 @@ from .inputs import (  # noqa: F401
     random_cases,
     poison_case,
     case_summary,
+    score_rows,
 )

@@ -480,3 +480,21 @@ def case_summary(case: MsaCase) -> dict:
         "Hkv": case.Hkv, "MB": case.max_blocks, "mode": case.sparse_mode,
         "init": case.init_blocks, "local": case.local_blocks, "poison": case.poison,
     }
+
+
+def score_rows(seed: int, Hq: int, T: int, W: int, ties: bool = True) -> torch.Tensor:
+    """Seeded float32 score rows [Hq, T, W] for the top-k selection: values
+    from a small pool (many exact ties, including the local_mask constants
+    1e30 and 1e29) with some normal noise, or all normal with ties=False;
+    about 20% -inf and 1% NaN entries."""
+    rng = np.random.default_rng(seed)
+    if ties:
+        pool = np.array([-3.5, -1.0, 0.0, 0.25, 2.0, 2.0, 7.75, 1e29, 1e30], dtype=np.float32)
+        s = rng.choice(pool, size=(Hq, T, W)).astype(np.float32)
+        s += (rng.choice([0, 0, 0, 1], size=s.shape).astype(np.float32) *
+              rng.standard_normal(s.shape).astype(np.float32))
+    else:
+        s = rng.standard_normal((Hq, T, W)).astype(np.float32)
+    s[rng.random(s.shape) < 0.2] = -np.inf
+    s[rng.random(s.shape) < 0.01] = np.nan
+    return torch.from_numpy(s)

@@ -203,3 +203,30 @@ def test_attribute_rules():
     assert call(q=q0, k=tnd, layout=0, table=None, mb=3, init=17) == ATTR
     assert call(family=2) == ATTR
     assert call(family=-2) == ATTR
+
+
+def test_block_topk_validation_without_launch():
+    # Every call below fails validation or has no rows, so nothing launches.
+    f = m.load_library().msa_block_topk
+    P = ctypes.c_void_p(FAKE)
+    assert f(P, 0, 5, 16, 16, 16, P, None) == OK          # Hq * T = 0
+    assert f(P, 3, 0, 16, 16, 16, P, None) == OK
+    assert f(None, 0, 0, 0, 0, 16, None, None) == OK
+    assert f(P, 2, 3, 16, 16, 0, P, None) == ATTR         # k out of [1, 64]
+    assert f(P, 2, 3, 16, 16, 65, P, None) == ATTR
+    assert f(P, 2, 3, 16, 17, 16, P, None) == SHAPE       # num_valid > width
+    assert f(P, 2, 3, 16, -1, 16, P, None) == SHAPE
+    assert f(P, -1, 3, 16, 4, 16, P, None) == SHAPE
+    assert f(P, 2, 3, (1 << 24) + 16, 4, 16, P, None) == SHAPE
+    assert f(None, 2, 3, 16, 4, 16, P, None) == NULL      # scores needed
+    assert f(P, 2, 3, 16, 4, 16, None, None) == NULL      # out needed
+    assert f(ctypes.c_void_p(FAKE + 2), 2, 3, 16, 4, 16, P, None) == STRIDE
+    assert f(P, 2, 3, 16, 4, 16, ctypes.c_void_p(FAKE + 1), None) == STRIDE
+
+
+def test_block_topk_binding_checks_shapes():
+    s = torch.zeros(2, 3, 16)
+    with pytest.raises(ValueError):
+        m.msa_block_topk(s, 16, 16, torch.zeros(3, 2, 8, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        m.msa_block_topk(s.double(), 16, 16, torch.zeros(3, 2, 16, dtype=torch.int32))

@@ -1,0 +1,131 @@
+"""Parity of the HIP top-k block selection (msa_block_topk, through the C ABI)
+with the CPU oracle.
+
+Integer work, so the bar is bit-exactness: on seeded score rows full of exact
+ties, -inf holes, NaN and the local_mask constants, and on the score rows the
+HIP path itself produces for every benchmark workload (so the selection runs
+on exactly the same floats on both sides).  Row lengths cover the register
+paths (up to 2048 blocks) and the re-reading path above it, with num_valid
+cutting rows short and k at its limits.  The full pipeline (GPU scores -> GPU
+top-k) is also compared with the oracle's own scores -> oracle top-k, where
+sets may differ only on blocks tied within the score tolerance.
+"""
+import sys
+
+import pytest
+import torch
+
+import oracle
+import synth
+from compare import TOL
+from test_parity_gpu import run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_max_qk_amd
+    block_max_qk_amd.load_library()
+    return torch.device("cuda:0")
+
+
+def gpu_topk(scores_cpu, dev, num_valid, k):
+    import block_max_qk_amd as m
+    s = scores_cpu.to(dev)
+    Hq, T, W = s.shape
+    out = torch.full((T, Hq, k), 777, dtype=torch.int32, device=dev)
+    m.msa_block_topk(s, num_valid, k, out)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("W", [1, 16, 100, 256, 512, 1000, 1024, 2048, 2100, 4112])
+@pytest.mark.parametrize("k", [1, 16, 64])
+def test_random_rows_exact(W, k, dev):
+    s = synth.score_rows(9000 + 3 * W + k, 3, 5, W)
+    for nv in sorted({0, W // 3, W}):
+        log(f"topk rows W={W} k={k} num_valid={nv}")
+        assert torch.equal(gpu_topk(s, dev, nv, k), oracle.block_topk(s, nv, k)), (W, k, nv)
+
+
+@pytest.mark.parametrize("ties", [True, False])
+def test_many_rows_exact(ties, dev):
+    s = synth.score_rows(31 if ties else 32, 8, 700, 512, ties=ties)
+    log(f"topk many rows ties={ties}")
+    assert torch.equal(gpu_topk(s, dev, 512, 16), oracle.block_topk(s, 512, 16))
+
+
+def test_degenerate_rows(dev):
+    W = 300
+    s = torch.full((2, 3, W), float("-inf"))
+    s[0, 0, 7] = 1.0                     # one candidate
+    s[0, 1, :] = 2.5                     # all tied: the lowest 16 indices
+    s[0, 2, :] = float("nan")            # nothing selectable
+    s[1, 0, ::2] = 1e30                  # more forced blocks than k
+    s[1, 1, 5:9] = 1e29                  # fewer forced blocks than k, rest -inf
+    s[1, 2, :] = torch.arange(W, dtype=torch.float32)   # strictly increasing
+    for k in (1, 16, 64):
+        log(f"topk degenerate k={k}")
+        assert torch.equal(gpu_topk(s, dev, W, k), oracle.block_topk(s, W, k))
+    assert gpu_topk(s, dev, 0, 16).eq(-1).all()
+
+
+def test_empty_sizes_launch_nothing(dev):
+    import block_max_qk_amd as m
+    for shape in ((0, 4, 16), (3, 0, 16)):
+        s = torch.zeros(shape, device=dev)
+        out = torch.empty((shape[1], shape[0], 16), dtype=torch.int32, device=dev)
+        m.msa_block_topk(s, 16, 16, out)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("c", range(len(synth.CONFIG_NAMES)), ids=synth.CONFIG_NAMES)
+def test_workload_scores_exact(c, dev):
+    case = synth.config_case(c)
+    log(f"topk on the GPU scores of {case.name}")
+    scores = run_gpu(case, dev)
+    Hq, T, W = scores.shape
+    got = gpu_topk(scores, dev, case.max_blocks, 16)
+    if Hq * T <= 4096:
+        want = oracle.block_topk(scores, case.max_blocks, 16)
+        assert torch.equal(got, want)
+        return
+    g = torch.Generator().manual_seed(77 + c)
+    rows = torch.randperm(Hq * T, generator=g)[:3000]
+    h, t = rows // T, rows % T
+    want = oracle.block_topk(scores[h, t][None], case.max_blocks, 16)[:, 0]
+    assert torch.equal(got[t, h], want)
+
+
+def test_pipeline_against_oracle_scores(dev):
+    # GPU scores -> GPU top-k against oracle scores -> oracle top-k: the sets
+    # may differ only where the oracle scores tie within the score tolerance
+    # of the k-th one.
+    for c in (0, 1):
+        case = synth.config_case(c)
+        log(f"topk pipeline {case.name}")
+        ref = oracle.index_score_case(case)
+        got = gpu_topk(run_gpu(case, dev), dev, case.max_blocks, 16)
+        want = oracle.block_topk(ref, case.max_blocks, 16)
+        Hq, T, W = ref.shape
+        fin = torch.isfinite(ref) & (ref.abs() < 1e28)
+        M = float(ref[fin].abs().max()) if fin.any() else 0.0
+        tau = TOL[case.key_dtype_name()] * M
+        bad = 0
+        for t in range(T):
+            for h in range(Hq):
+                a = set(int(x) for x in got[t, h] if x >= 0)
+                b = set(int(x) for x in want[t, h] if x >= 0)
+                if a == b:
+                    continue
+                kth = min(float(ref[h, t, x]) for x in b)
+                if any(abs(float(ref[h, t, x]) - kth) > tau for x in a ^ b):
+                    bad += 1
+        assert bad == 0, f"{case.name}: {bad} rows differ beyond near ties"

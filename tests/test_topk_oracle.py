@@ -21,6 +21,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 
 NINF = float("-inf")
 
@@ -45,18 +46,7 @@ def rank_brute(scores: np.ndarray, num_valid: int, k: int) -> np.ndarray:
 
 
 def random_scores(rng, Hq, T, W, tie_pool=True):
-    """Rows with many exact ties, -inf holes, forced-block constants and
-    the odd NaN."""
-    if tie_pool:
-        pool = np.array([-3.5, -1.0, 0.0, 0.25, 2.0, 2.0, 7.75, 1e29, 1e30], dtype=np.float32)
-        s = rng.choice(pool, size=(Hq, T, W)).astype(np.float32)
-        s += rng.choice([0, 0, 0, 1], size=s.shape).astype(np.float32) * \
-            rng.standard_normal(s.shape).astype(np.float32)
-    else:
-        s = rng.standard_normal((Hq, T, W)).astype(np.float32)
-    s[rng.random(s.shape) < 0.2] = NINF
-    s[rng.random(s.shape) < 0.01] = np.nan
-    return s
+    return synth.score_rows(int(rng.integers(1 << 30)), Hq, T, W, ties=tie_pool).numpy()
 
 
 @pytest.mark.parametrize("W", [1, 16, 48, 257])
