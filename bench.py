@@ -15,6 +15,9 @@ is replicated into several HBM copies and the steps rotate over them.
 
 Output: one JSON line (rank 0 of 1).  ``--config all`` prints one line per
 workload instead (for measurement; the default line is the headline).
+``--topk`` times the top-k block selection (msa_block_topk, k = 16) over the
+chosen workload's score rows instead, with its own roofline (HBM bytes: every
+row's num_valid scores read, its k indices written).
 """
 from __future__ import annotations
 
@@ -242,6 +245,83 @@ def cpu_baseline_leg(case, stats, args) -> dict:
             f"block scores in {dt:.2f} s"}
 
 
+TOPK_METRIC = "top-k block selections/s (k=16) + achieved HBM GB/s, 1 GPU"
+
+
+def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) -> dict:
+    """Time msa_block_topk (k = 16) on the score rows of a workload: the
+    scores are computed once by the operator, then each step is one top-k
+    launch over all [Hq, T] rows (inputs resident in HBM; the prefill score
+    tensors are ~1 GB, beyond the Infinity Cache)."""
+    import torch
+    import block_max_qk_amd as m
+    import synth
+
+    dev = torch.device("cuda:0")
+    k = 16
+    case = synth.config_case(c_idx)
+    W = m.msa_index_score_out_width(case.max_blocks)
+    d = dict(query=case.query.to(dev), key=case.key_storage.to(dev))
+    key = d["key"][:: case.gap + 1] if case.gap else d["key"]
+    scores = torch.empty((case.Hq, case.T, W), dtype=torch.float32, device=dev)
+    m.msa_index_score(d["query"], key, case.start_loc.to(dev),
+                      None if case.block_table is None else case.block_table.to(dev),
+                      None if case.scale is None else case.scale.to(dev),
+                      case.cu_seqlens_q.to(dev), case.kv_len.to(dev), case.layout,
+                      case.sparse_mode, case.init_blocks, case.local_blocks, scores,
+                      case.max_blocks)
+    del d, key
+    nv = case.max_blocks
+    rows = case.Hq * case.T
+    out = torch.empty((case.T, case.Hq, k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        m.msa_block_topk(scores, nv, k, out, stream=stream)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev0[i].record(stream)
+        m.msa_block_topk(scores, nv, k, out, stream=stream)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
+    kernel_ms = sum(kms) / len(kms)
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    alg = rows * (nv + k) * 4      # each row's num_valid scores read, k indices written
+    gbs = alg / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "metric": TOPK_METRIC, "value": round(rows / (ms_per_step * 1e-3), 1),
+        "unit": "block selections/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": case.name, "stage": "top-k", "k": k, "rows": rows,
+                   "width": W, "num_valid": nv},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "topk_kernel", "kernel_ms_avg": round(kernel_ms, 5),
+                     "kernel_ms_median": round(kms[len(kms) // 2], 5),
+                     "algorithmic_bytes": alg},
+        "cpu_baseline": None,
+    }
+    if cpu_baseline:
+        import oracle
+        import torch as _t
+        g = _t.Generator().manual_seed(7)
+        n = min(rows, args.cpu_topk_rows)
+        pick = _t.randperm(rows, generator=g)[:n]
+        sample = scores.reshape(rows, W)[pick.to(dev)].cpu()[None]
+        t = time.perf_counter()
+        oracle.block_topk(sample, nv, k)
+        dt = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": round(n / dt, 1), "unit": "block selections/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{n} random rows of the workload in {dt:.2f} s"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +334,9 @@ def main():
     ap.add_argument("--family", type=int, default=-1, help="-1 auto, 0 decode, 1 prefill tiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--topk", action="store_true",
+                    help="time the top-k block selection on the workload's scores instead")
+    ap.add_argument("--cpu-topk-rows", type=int, default=200000)
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the operator, run this many MiB device copies "
                          "(counter calibration)")
@@ -291,6 +374,10 @@ def main():
     else:
         todo = [names.index(args.config)]
     for c in todo:
+        if args.topk:
+            print(json.dumps(bench_topk(c, args.steps, args.warmup, not args.no_cpu_baseline,
+                                        args)), flush=True)
+            continue
         copies = args.copies
         if copies <= 0:
             copies = 4 if c in (1, 3) else 1

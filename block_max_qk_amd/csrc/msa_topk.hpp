@@ -11,12 +11,14 @@
 // One wave per row.  Scores map to order-preserving 32-bit keys (0 for blocks
 // that cannot be selected); the k-th largest key tau is found bit by bit from
 // the top, each step counting the keys at or above a candidate threshold with
-// wave ballots (the counts stay in scalar registers).  The selection is then
-// compacted in index order: every key above tau, and keys equal to tau while
-// slots remain, lowest index first -- which also yields the ascending output
-// without a sort.  Rows of up to 64 * J blocks keep their keys in registers
-// (read once, 256 contiguous bytes per load instruction); longer rows (J = 0)
-// re-read the row, from L2, at every step.
+// wave ballots.  As soon as at most 64 keys remain at or
+// above the threshold being built, they move (in index order) into one
+// register per lane and the rest of the search runs on that register alone.
+// The selection is compacted in index order: every key above tau, and keys
+// equal to tau while slots remain, lowest index first -- which also yields the
+// ascending output without a sort.  Rows of up to 64 * J blocks keep their
+// keys in registers (read once, 256 contiguous bytes per load instruction);
+// longer rows (J = 0) re-read the row, from L2, at every step.
 #pragma once
 
 #include "msa_device.hpp"
@@ -70,27 +72,71 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     return n;
   };
 
-  // tau = the k-th largest key, or 0 when the row has at most k candidates
+  // tau = the k-th largest key, or 0 when the row has at most k candidates.
+  // Once at most 64 keys remain at or above tau, they are compacted in index
+  // order into one register per lane (through a per-wave LDS slot), and the
+  // remaining steps and the selection work on that register alone.
+  __shared__ uint2 packed[4][64];
+  uint2* const slot = packed[threadIdx.x >> 6];
+  const uint64_t below = (1ull << l) - 1ull;
   uint32_t tau = 0;
-  if (count_ge(1u) > k) {
+  bool comp = false;
+  uint32_t ck = 0;            // compacted key (0 in lanes past the count)
+  int ci = -1;                // its block index
+  auto compact = [&]() {
+    int base = 0;
+    for (int j = 0; j < nj; ++j) {
+      const uint32_t kv = key(j);
+      const uint64_t m = __ballot(kv >= tau);
+      if (kv >= tau) slot[base + __popcll(m & below)] = make_uint2(kv, j * 64 + l);
+      base += __popcll(m);
+    }
+    wave_lds_sync();
+    const uint2 e = slot[l];
+    ck = l < base ? e.x : 0u;
+    ci = l < base ? (int)e.y : -1;
+    comp = true;
+  };
+  int cnt = count_ge(1u);     // keys >= tau (tau = 0: the candidates)
+  if (cnt > k) {
+    if (cnt <= 64) {
+      tau = 1u;
+      compact();
+      tau = 0u;
+    }
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = tau | (1u << bit);
-      if (count_ge(c) >= k) tau = c;
+      const int n = comp ? __popcll(__ballot(ck >= c)) : count_ge(c);
+      if (n >= k) {
+        tau = c;
+        cnt = n;
+        if (!comp && cnt <= 64) compact();
+      }
     }
   }
   // keys above tau all fit; ties at tau fill the remaining slots
-  const int need_eq = tau == 0 ? 0 : k - count_ge(tau + 1u);
-  const uint64_t below = (1ull << l) - 1ull;
-  int taken = 0, eq_seen = 0;
-  for (int j = 0; j < nj; ++j) {
-    const uint32_t kv = key(j);
-    const bool eq = tau != 0u && kv == tau;
+  int taken = 0;
+  if (comp) {
+    const int need_eq = k - __popcll(__ballot(ck > tau));
+    const bool eq = ck == tau;
     const uint64_t em = __ballot(eq);
-    const bool take = kv > tau || (eq && eq_seen + __popcll(em & below) < need_eq);
+    const bool take = ck > tau || (eq && __popcll(em & below) < need_eq);
     const uint64_t tm = __ballot(take);
-    if (take) dst[taken + __popcll(tm & below)] = j * 64 + l;
-    taken += __popcll(tm);
-    eq_seen += __popcll(em);
+    if (take) dst[__popcll(tm & below)] = ci;
+    taken = __popcll(tm);
+  } else {
+    const int need_eq = tau == 0 ? 0 : k - count_ge(tau + 1u);
+    int eq_seen = 0;
+    for (int j = 0; j < nj; ++j) {
+      const uint32_t kv = key(j);
+      const bool eq = tau != 0u && kv == tau;
+      const uint64_t em = __ballot(eq);
+      const bool take = kv > tau || (eq && eq_seen + __popcll(em & below) < need_eq);
+      const uint64_t tm = __ballot(take);
+      if (take) dst[taken + __popcll(tm & below)] = j * 64 + l;
+      taken += __popcll(tm);
+      eq_seen += __popcll(em);
+    }
   }
   if (l < k && l >= taken) dst[l] = -1;
 }
