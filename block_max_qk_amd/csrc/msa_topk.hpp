@@ -83,34 +83,44 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   bool comp = false;
   uint32_t ck = 0;            // compacted key (0 in lanes past the count)
   int ci = -1;                // its block index
-  auto compact = [&]() {
-    int base = 0;
-    for (int j = 0; j < nj; ++j) {
-      const uint32_t kv = key(j);
-      const uint64_t m = __ballot(kv >= tau);
-      if (kv >= tau) slot[base + __popcll(m & below)] = make_uint2(kv, j * 64 + l);
-      base += __popcll(m);
-    }
-    wave_lds_sync();
-    const uint2 e = slot[l];
-    ck = l < base ? e.x : 0u;
-    ci = l < base ? (int)e.y : -1;
-    comp = true;
-  };
-  int cnt = count_ge(1u);     // keys >= tau (tau = 0: the candidates)
+  int cnt = count_ge(1u);     // keys >= tau, tau = 0: the candidates
   if (cnt > k) {
-    if (cnt <= 64) {
-      tau = 1u;
-      compact();
-      tau = 0u;
+    // phase 1: bits from the top while more than 64 keys reach tau
+    int bit = 31;
+    if (cnt > 64) {
+      for (; bit >= 0; --bit) {
+        const uint32_t c = tau | (1u << bit);
+        const int n = count_ge(c);
+        if (n >= k) {
+          tau = c;
+          cnt = n;
+          if (n <= 64) {
+            --bit;
+            break;
+          }
+        }
+      }
     }
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = tau | (1u << bit);
-      const int n = comp ? __popcll(__ballot(ck >= c)) : count_ge(c);
-      if (n >= k) {
-        tau = c;
-        cnt = n;
-        if (!comp && cnt <= 64) compact();
+    // the keys reaching tau (all candidates when tau is still 0), in index
+    // order, one per lane
+    if (cnt <= 64) {
+      const uint32_t floor_key = tau == 0u ? 1u : tau;
+      int base = 0;
+      for (int j = 0; j < nj; ++j) {
+        const uint32_t kv = key(j);
+        const uint64_t m = __ballot(kv >= floor_key);
+        if (kv >= floor_key) slot[base + __popcll(m & below)] = make_uint2(kv, j * 64 + l);
+        base += __popcll(m);
+      }
+      wave_lds_sync();
+      const uint2 e = slot[l];
+      ck = l < base ? e.x : 0u;
+      ci = l < base ? (int)e.y : -1;
+      comp = true;
+      // phase 2: the remaining bits on that register alone
+      for (; bit >= 0; --bit) {
+        const uint32_t c = tau | (1u << bit);
+        if (__popcll(__ballot(ck >= c)) >= k) tau = c;
       }
     }
   }
