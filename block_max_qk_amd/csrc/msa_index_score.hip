@@ -287,29 +287,29 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   if (Hq < 0 || T < 0 || width < 0 || width > (1 << 24) || num_valid < 0 || num_valid > width)
     return MSA_ERR_SHAPE;
   if (k < 1 || k > msa::kTopkMax) return MSA_ERR_ATTR;
-  if (Hq > 0 && T > INT64_MAX / Hq) return MSA_ERR_SHAPE;
-  const int64_t rows = Hq * T;
-  if (rows == 0) return MSA_OK;
-  if (rows > (int64_t)INT32_MAX * 4) return MSA_ERR_SHAPE;
+  if (Hq == 0 || T == 0) return MSA_OK;
+  // grid (ceil(T / 4), Hq), one row per wave
+  if (Hq > 65535 || (T + 3) / 4 > INT32_MAX || T > INT64_MAX / Hq / std::max<int64_t>(width, 1))
+    return MSA_ERR_SHAPE;
   if (!out || (num_valid > 0 && !scores)) return MSA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
     return MSA_ERR_STRIDE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const dim3 grid((unsigned)((T + 3) / 4), (unsigned)Hq), block(256);
   const int nv = (int)num_valid;
   // keys of up to 64 * J blocks stay in registers; longer rows are re-read
   if (nv <= 128)
-    hipLaunchKernelGGL(msa::topk_kernel<2>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL(msa::topk_kernel<2>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
   else if (nv <= 256)
-    hipLaunchKernelGGL(msa::topk_kernel<4>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL(msa::topk_kernel<4>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
   else if (nv <= 512)
-    hipLaunchKernelGGL(msa::topk_kernel<8>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL(msa::topk_kernel<8>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
   else if (nv <= 1024)
-    hipLaunchKernelGGL(msa::topk_kernel<16>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL(msa::topk_kernel<16>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
   else if (nv <= 2048)
-    hipLaunchKernelGGL(msa::topk_kernel<32>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL(msa::topk_kernel<32>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
   else
-    hipLaunchKernelGGL(msa::topk_kernel<0>, grid, block, 0, s, scores, rows, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL(msa::topk_kernel<0>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 

@@ -34,35 +34,44 @@ __device__ __forceinline__ uint32_t topk_key(float f) {
   return f > -__builtin_inff() ? key : 0u;
 }
 
+// All ones when b < n, else 0 (arithmetic, so no branch forms around it).
+__device__ __forceinline__ uint32_t below_mask(int b, int n) { return (uint32_t)((b - n) >> 31); }
+
 template <int J>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
-                                                   int64_t rows, int64_t T, int64_t Hq,
-                                                   int64_t W, int nv, int k,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, int64_t T,
+                                                   int64_t Hq, int64_t W, int nv, int k,
                                                    int32_t* __restrict__ out) {
   const int l = lane_id();
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row h * T + t
-  if (r >= rows) return;
-  const float* row = scores + r * W;
-  const int64_t h = r / T;
-  const int64_t t = r - h * T;
+  // grid (ceil(T / 4), Hq): wave w of block (x, h) takes row (h, t = 4x + w)
+  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t h = blockIdx.y;
   int32_t* const dst = out + (t * Hq + h) * k;
+  if (nv == 0) {                           // nothing to select; scores may be NULL
+    if (l < k) dst[l] = -1;
+    return;
+  }
+  const float* row = scores + (h * T + t) * W;
   const int nch = (nv + 63) / 64;          // 64-block chunks holding candidates
   const int nj = J > 0 ? J : nch;
 
+  // Every lane loads, at its block index clamped into [0, nv), and blocks
+  // past nv are masked afterwards: the loads carry no branch, so all of a
+  // row's loads are in flight together.
   uint32_t keys[J > 0 ? J : 1];
   if constexpr (J > 0) {
+    float v[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int b = j * 64 + l;
-      keys[j] = b < nv ? topk_key(__builtin_nontemporal_load(row + b)) : 0u;
-    }
+    for (int j = 0; j < J; ++j) v[j] = __builtin_nontemporal_load(row + min(j * 64 + l, nv - 1));
+#pragma unroll
+    for (int j = 0; j < J; ++j) keys[j] = topk_key(v[j]) & below_mask(j * 64 + l, nv);
   }
   auto key = [&](int j) -> uint32_t {
     if constexpr (J > 0) {
       return keys[j];
     } else {
       const int b = j * 64 + l;
-      return b < nv ? topk_key(row[b]) : 0u;
+      return topk_key(row[min(b, nv - 1)]) & below_mask(b, nv);
     }
   };
   // number of keys >= c over the row

@@ -159,7 +159,8 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
  *
  * scores     device float32 [Hq, T, width], compact (msa_index_score's out),
  *            4-byte aligned; not read when num_valid = 0.
- * Hq, T, width  sizes, >= 0, width <= 2^24.
+ * Hq, T, width  sizes, >= 0, Hq <= 65535, T <= 2^33, width <= 2^24, and
+ *            Hq * T * width below 2^63.
  * num_valid  blocks to consider, in [0, width] (the table width MB for an
  *            msa_index_score output; columns past it are padding).
  * k          1..64 (the sparse_topk_select contract uses 16).
@@ -167,10 +168,10 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
  * stream     hipStream_t (as void*); the call is asynchronous on it.
  *
  * Ownership: caller-owned pointers; nothing is allocated or kept.  Returns
- * MSA_OK (also, without launching, when Hq * T = 0), MSA_ERR_SHAPE for sizes
- * out of range, MSA_ERR_ATTR for k out of range, MSA_ERR_NULL for a NULL
- * pointer the call must use, MSA_ERR_STRIDE for a misaligned one,
- * MSA_ERR_HIP if the launch fails. */
+ * MSA_OK (also, without launching or checking pointers, when Hq * T = 0),
+ * MSA_ERR_SHAPE for sizes out of range, MSA_ERR_ATTR for k out of range,
+ * MSA_ERR_NULL for a NULL pointer the call must use, MSA_ERR_STRIDE for a
+ * misaligned one, MSA_ERR_HIP if the launch fails. */
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
                             int64_t num_valid, int32_t k, int32_t* out, void* stream);
 

@@ -218,6 +218,9 @@ def test_block_topk_validation_without_launch():
     assert f(P, 2, 3, 16, -1, 16, P, None) == SHAPE
     assert f(P, -1, 3, 16, 4, 16, P, None) == SHAPE
     assert f(P, 2, 3, (1 << 24) + 16, 4, 16, P, None) == SHAPE
+    assert f(P, 65536, 3, 16, 4, 16, P, None) == SHAPE    # Hq is the grid's y extent
+    assert f(P, 2, 1 << 34, 16, 4, 16, P, None) == SHAPE  # ceil(T / 4) blocks in x
+    assert f(P, 1 << 14, 1 << 30, 1 << 24, 4, 16, P, None) == SHAPE   # element count
     assert f(None, 2, 3, 16, 4, 16, P, None) == NULL      # scores needed
     assert f(P, 2, 3, 16, 4, 16, None, None) == NULL      # out needed
     assert f(ctypes.c_void_p(FAKE + 2), 2, 3, 16, 4, 16, P, None) == STRIDE
