@@ -75,6 +75,31 @@ __device__ __forceinline__ T wave_incl_scan(T x) {
   return x;
 }
 
+// Value of another lane in the same row of 16, by a DPP lane pattern.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Smallest and largest value over the whole wave (every lane active): within
+// each row of 16 lanes by swapping neighbours, then quads, then mirroring
+// half rows and rows; then over the four rows.
+__device__ __forceinline__ void wave_min_max(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  uint32_t a = v, b = v;
+  a = min(a, dpp_u32<0xB1>(a));    // quad_perm 1,0,3,2
+  b = max(b, dpp_u32<0xB1>(b));
+  a = min(a, dpp_u32<0x4E>(a));    // quad_perm 2,3,0,1
+  b = max(b, dpp_u32<0x4E>(b));
+  a = min(a, dpp_u32<0x141>(a));   // row_half_mirror
+  b = max(b, dpp_u32<0x141>(b));
+  a = min(a, dpp_u32<0x140>(a));   // row_mirror
+  b = max(b, dpp_u32<0x140>(b));
+  lo = min(min((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 16)),
+           min((uint32_t)__builtin_amdgcn_readlane((int)a, 32), (uint32_t)__builtin_amdgcn_readlane((int)a, 48)));
+  hi = max(max((uint32_t)__builtin_amdgcn_readlane((int)b, 0), (uint32_t)__builtin_amdgcn_readlane((int)b, 16)),
+           max((uint32_t)__builtin_amdgcn_readlane((int)b, 32), (uint32_t)__builtin_amdgcn_readlane((int)b, 48)));
+}
+
 __device__ __forceinline__ i32x4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }

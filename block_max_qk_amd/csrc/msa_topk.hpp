@@ -81,10 +81,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     return n;
   };
 
-  // tau = the k-th largest key, or 0 when the row has at most k candidates.
-  // Once at most 64 keys remain at or above tau, they are compacted in index
-  // order into one register per lane (through a per-wave LDS slot), and the
-  // remaining steps and the selection work on that register alone.
+  // tau = the k-th largest key (0 when the row has at most k candidates), or
+  // any lower threshold that exactly k keys reach: the search stops there.
+  // Once at most 64 keys reach tau, they are compacted in index order into
+  // one register per lane (through a per-wave LDS slot), and the remaining
+  // steps and the selection work on that register alone.
   __shared__ uint2 packed[4][64];
   uint2* const slot = packed[threadIdx.x >> 6];
   const uint64_t below = (1ull << l) - 1ull;
@@ -94,9 +95,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   int ci = -1;                // its block index
   int cnt = count_ge(1u);     // keys >= tau, tau = 0: the candidates
   if (cnt > k) {
-    // phase 1: bits from the top while more than 64 keys reach tau
     int bit = 31;
     if (cnt > 64) {
+      if constexpr (J > 0) {
+        // With a candidate in every lane, tau lies between the smallest lane
+        // maximum (64 keys reach it) and the largest key, so it has the
+        // leading bits those two share; the search starts below them.
+        uint32_t mx = keys[0];
+#pragma unroll
+        for (int j = 1; j < J; ++j) mx = max(mx, keys[j]);
+        uint32_t lo, hi;
+        wave_min_max(mx, lo, hi);
+        if (lo == hi) {
+          tau = lo;
+          bit = -1;
+        } else if (lo != 0u) {
+          bit = 31 - __builtin_clz(lo ^ hi);
+          tau = hi & ~((2u << bit) - 1u);
+        }
+      }
+      // phase 1: count over all chunks while more than 64 keys reach tau
       for (; bit >= 0; --bit) {
         const uint32_t c = tau | (1u << bit);
         const int n = count_ge(c);
@@ -127,9 +145,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       ci = l < base ? (int)e.y : -1;
       comp = true;
       // phase 2: the remaining bits on that register alone
-      for (; bit >= 0; --bit) {
+      for (; bit >= 0 && cnt > k; --bit) {
         const uint32_t c = tau | (1u << bit);
-        if (__popcll(__ballot(ck >= c)) >= k) tau = c;
+        const int n = __popcll(__ballot(ck >= c));
+        if (n >= k) {
+          tau = c;
+          cnt = n;
+        }
       }
     }
   }
