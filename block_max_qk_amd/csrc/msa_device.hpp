@@ -81,11 +81,11 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
-// Smallest and largest value over the whole wave (every lane active): within
-// each row of 16 lanes by swapping neighbours, then quads, then mirroring
-// half rows and rows; then over the four rows.
-__device__ __forceinline__ void wave_min_max(uint32_t v, uint32_t& lo, uint32_t& hi) {
-  uint32_t a = v, b = v;
+// Smallest value of x and largest value of y over the whole wave (every
+// lane active): within each row of 16 lanes by swapping neighbours, then
+// quads, then mirroring half rows and rows; then over the four rows.
+__device__ __forceinline__ void wave_min_max(uint32_t x, uint32_t y, uint32_t& lo, uint32_t& hi) {
+  uint32_t a = x, b = y;
   a = min(a, dpp_u32<0xB1>(a));    // quad_perm 1,0,3,2
   b = max(b, dpp_u32<0xB1>(b));
   a = min(a, dpp_u32<0x4E>(a));    // quad_perm 2,3,0,1
@@ -94,10 +94,9 @@ __device__ __forceinline__ void wave_min_max(uint32_t v, uint32_t& lo, uint32_t&
   b = max(b, dpp_u32<0x141>(b));
   a = min(a, dpp_u32<0x140>(a));   // row_mirror
   b = max(b, dpp_u32<0x140>(b));
-  lo = min(min((uint32_t)__builtin_amdgcn_readlane((int)a, 0), (uint32_t)__builtin_amdgcn_readlane((int)a, 16)),
-           min((uint32_t)__builtin_amdgcn_readlane((int)a, 32), (uint32_t)__builtin_amdgcn_readlane((int)a, 48)));
-  hi = max(max((uint32_t)__builtin_amdgcn_readlane((int)b, 0), (uint32_t)__builtin_amdgcn_readlane((int)b, 16)),
-           max((uint32_t)__builtin_amdgcn_readlane((int)b, 32), (uint32_t)__builtin_amdgcn_readlane((int)b, 48)));
+  auto lane = [](uint32_t v, int i) { return (uint32_t)__builtin_amdgcn_readlane((int)v, i); };
+  lo = min(min(lane(a, 0), lane(a, 16)), min(lane(a, 32), lane(a, 48)));
+  hi = max(max(lane(b, 0), lane(b, 16)), max(lane(b, 32), lane(b, 48)));
 }
 
 __device__ __forceinline__ i32x4 ld16(const uint8_t* p) {

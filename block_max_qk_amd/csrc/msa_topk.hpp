@@ -83,60 +83,97 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 
   // tau = the k-th largest key (0 when the row has at most k candidates), or
   // any lower threshold that exactly k keys reach: the search stops there.
-  // Once at most 64 keys reach tau, they are compacted in index order into
-  // one register per lane (through a per-wave LDS slot), and the remaining
-  // steps and the selection work on that register alone.
-  __shared__ uint2 packed[4][64];
+  // Invariant: at least k keys reach tau, and the bits of tau above `bit`
+  // are final.  Once at most 64 keys reach tau, they are compacted in index
+  // order into one register per lane (through a per-wave LDS slot), and the
+  // remaining steps and the selection work on that register alone.
+  __shared__ uint2 packed[4][128];
   uint2* const slot = packed[threadIdx.x >> 6];
-  const uint64_t below = (1ull << l) - 1ull;
   uint32_t tau = 0;
   bool comp = false;
   uint32_t ck = 0;            // compacted key (0 in lanes past the count)
   int ci = -1;                // its block index
   int cnt = count_ge(1u);     // keys >= tau, tau = 0: the candidates
+  uint32_t mb = 0x80000000u;   // the bit of tau under test; 0 once all are final
+  // With lb <= (the final tau) <= ub and tau <= lb: every value in [lb, ub]
+  // has the leading bits lb and ub share, so tau takes them and the search
+  // goes on below them.
+  auto narrow = [&](uint32_t lb, uint32_t ub) {
+    if (lb >= ub) {
+      tau = ub;
+      mb = 0u;
+    } else {
+      mb = 0x80000000u >> __builtin_clz(lb ^ ub);
+      tau = ub & ~(2u * mb - 1u);
+    }
+  };
   if (cnt > k) {
-    int bit = 31;
     if (cnt > 64) {
+      // phase 1: counts over all chunks while more than 64 keys reach tau.
+      // With a candidate in every lane, the smallest lane maximum lo is a
+      // lower bound (64 keys reach it) and the largest key an upper one.  At
+      // the first threshold c that fewer than k keys reach, the largest key
+      // below c is the tighter upper bound (it skips the few forced blocks
+      // far above the rest).
+      uint32_t lo = 0u;
       if constexpr (J > 0) {
-        // With a candidate in every lane, tau lies between the smallest lane
-        // maximum (64 keys reach it) and the largest key, so it has the
-        // leading bits those two share; the search starts below them.
         uint32_t mx = keys[0];
 #pragma unroll
         for (int j = 1; j < J; ++j) mx = max(mx, keys[j]);
-        uint32_t lo, hi;
-        wave_min_max(mx, lo, hi);
-        if (lo == hi) {
-          tau = lo;
-          bit = -1;
-        } else if (lo != 0u) {
-          bit = 31 - __builtin_clz(lo ^ hi);
-          tau = hi & ~((2u << bit) - 1u);
-        }
+        uint32_t hi;
+        wave_min_max(mx, mx, lo, hi);
+        if (lo != 0u) narrow(lo, hi);
       }
-      // phase 1: count over all chunks while more than 64 keys reach tau
-      for (; bit >= 0; --bit) {
-        const uint32_t c = tau | (1u << bit);
+      // steps up to the first threshold fewer than k keys reach
+      uint32_t c = 0u;
+      bool failed = false;
+      while (mb != 0u) {
+        c = tau | mb;
         const int n = count_ge(c);
-        if (n >= k) {
-          tau = c;
-          cnt = n;
-          if (n <= 64) {
-            --bit;
-            break;
-          }
+        if (n < k) {
+          failed = true;
+          break;
+        }
+        tau = c;
+        cnt = n;
+        mb >>= 1;
+        if (n <= 64) break;
+      }
+      if (failed) {
+        if constexpr (J > 0) {
+          uint32_t m2 = 0u;
+#pragma unroll
+          for (int j = 0; j < J; ++j) m2 = max(m2, keys[j] < c ? keys[j] : 0u);
+          uint32_t unused, hi2;
+          wave_min_max(m2, m2, unused, hi2);
+          narrow(max(lo, tau), hi2);
+        } else {
+          mb >>= 1;
+        }
+        while (mb != 0u) {
+          c = tau | mb;
+          const int n = count_ge(c);
+          const bool ok = n >= k;
+          tau = ok ? c : tau;
+          cnt = ok ? n : cnt;
+          mb >>= 1;
+          if (cnt <= 64) break;
         }
       }
     }
     // the keys reaching tau (all candidates when tau is still 0), in index
-    // order, one per lane
+    // order, one per lane; lanes whose key does not qualify write to the
+    // spare half of the slot, so the stores need no branch
     if (cnt <= 64) {
       const uint32_t floor_key = tau == 0u ? 1u : tau;
       int base = 0;
       for (int j = 0; j < nj; ++j) {
         const uint32_t kv = key(j);
-        const uint64_t m = __ballot(kv >= floor_key);
-        if (kv >= floor_key) slot[base + __popcll(m & below)] = make_uint2(kv, j * 64 + l);
+        const bool q = kv >= floor_key;
+        const uint64_t m = __ballot(q);
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        slot[q ? base + rank : 64 + l] = make_uint2(kv, j * 64 + l);
         base += __popcll(m);
       }
       wave_lds_sync();
@@ -144,18 +181,38 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       ck = l < base ? e.x : 0u;
       ci = l < base ? (int)e.y : -1;
       comp = true;
-      // phase 2: the remaining bits on that register alone
-      for (; bit >= 0 && cnt > k; --bit) {
-        const uint32_t c = tau | (1u << bit);
-        const int n = __popcll(__ballot(ck >= c));
-        if (n >= k) {
+      // phase 2: the remaining bits on that register alone, stopping as soon
+      // as exactly k keys reach tau, with the same refinement (the smallest
+      // compacted key is a lower bound)
+      if (cnt > k) {
+        uint32_t c = 0u;
+        bool failed = false;
+        while (mb != 0u) {
+          c = tau | mb;
+          const int n = __popcll(__ballot(ck >= c));
+          if (n < k) {
+            failed = true;
+            break;
+          }
           tau = c;
-          cnt = n;
+          mb = n == k ? 0u : mb >> 1;
+        }
+        if (failed) {
+          uint32_t lo2, hi2;
+          wave_min_max(ck != 0u ? ck : ~0u, ck < c ? ck : 0u, lo2, hi2);
+          narrow(max(lo2, tau), hi2);
+          while (mb != 0u) {
+            c = tau | mb;
+            const int n = __popcll(__ballot(ck >= c));
+            tau = n >= k ? c : tau;
+            mb = n == k ? 0u : mb >> 1;
+          }
         }
       }
     }
   }
   // keys above tau all fit; ties at tau fill the remaining slots
+  const uint64_t below = (1ull << l) - 1ull;
   int taken = 0;
   if (comp) {
     const int need_eq = k - __popcll(__ballot(ck > tau));
