@@ -295,21 +295,37 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(out) & 3u))
     return MSA_ERR_STRIDE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((T + 3) / 4), (unsigned)Hq), block(256);
   const int nv = (int)num_valid;
-  // keys of up to 64 * J blocks stay in registers; longer rows are re-read
+  // Keys of up to 64 * J blocks stay in registers, longer rows are re-read.
+  // With many rows a wave takes R = 2 of them in turn (the second row's
+  // loads overlap the selection on the first); few rows keep one per wave,
+  // for parallelism.
+  const bool many = Hq * T >= (int64_t)msa::kTopkManyRows && nv <= 2048;
+  const int R = many ? 2 : 1;
+  const dim3 grid((unsigned)((T + msa::kTopkWaves * R - 1) / (msa::kTopkWaves * R)), (unsigned)Hq);
+  const dim3 block(64 * msa::kTopkWaves);
+#define MSA_TOPK_LAUNCH(J)                                                                         \
+  do {                                                                                             \
+    if (many)                                                                                      \
+      hipLaunchKernelGGL((msa::topk_kernel<J, 2>), grid, block, 0, s, scores, T, Hq, width, nv, k,  \
+                         out);                                                                     \
+    else                                                                                           \
+      hipLaunchKernelGGL((msa::topk_kernel<J, 1>), grid, block, 0, s, scores, T, Hq, width, nv, k,  \
+                         out);                                                                     \
+  } while (0)
   if (nv <= 128)
-    hipLaunchKernelGGL(msa::topk_kernel<2>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    MSA_TOPK_LAUNCH(2);
   else if (nv <= 256)
-    hipLaunchKernelGGL(msa::topk_kernel<4>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    MSA_TOPK_LAUNCH(4);
   else if (nv <= 512)
-    hipLaunchKernelGGL(msa::topk_kernel<8>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    MSA_TOPK_LAUNCH(8);
   else if (nv <= 1024)
-    hipLaunchKernelGGL(msa::topk_kernel<16>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    MSA_TOPK_LAUNCH(16);
   else if (nv <= 2048)
-    hipLaunchKernelGGL(msa::topk_kernel<32>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    MSA_TOPK_LAUNCH(32);
   else
-    hipLaunchKernelGGL(msa::topk_kernel<0>, grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    hipLaunchKernelGGL((msa::topk_kernel<0, 1>), grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+#undef MSA_TOPK_LAUNCH
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 

@@ -8,8 +8,9 @@
 // index, written to out[t, h, 0:k] in ascending block order with a -1 tail.
 // It works on the raw scores (no exp or normalisation).
 //
-// One wave per row.  Scores map to order-preserving 32-bit keys (0 for blocks
-// that cannot be selected); the k-th largest key tau is found bit by bit from
+// One wave per row at a time (with many rows a wave takes two in turn,
+// loading the second while it selects on the first).  Scores map to order-preserving 32-bit keys (0 for
+// blocks that cannot be selected); the k-th largest key tau is found bit by bit from
 // the top, each step counting the keys at or above a candidate threshold with
 // wave ballots.  As soon as at most 64 keys remain at or
 // above the threshold being built, they move (in index order) into one
@@ -37,32 +38,29 @@ __device__ __forceinline__ uint32_t topk_key(float f) {
 // All ones when b < n, else 0 (arithmetic, so no branch forms around it).
 __device__ __forceinline__ uint32_t below_mask(int b, int n) { return (uint32_t)((b - n) >> 31); }
 
+constexpr int kTopkWaves = 4;  // waves per workgroup
+// Fourth word of a raw buffer descriptor on this architecture (32-bit data
+// format; stride 0 makes the size a byte count checked per access).
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer access: the nontemporal bit.
+constexpr int kCachePolicyNT = 2;
+// From this many rows on, each wave takes two rows in turn.
+constexpr int64_t kTopkManyRows = 65536;
+
+// The selection on one row whose scores (J > 0) are already in v: v[j] in
+// lane l holds block 64 j + l (any value past nv).  J = 0 re-reads the row.
+// slot: this wave's 128-entry LDS area; sel: its 64-entry output area.  The
+// k results go to dst with one store per lane (lanes past k repeat slot k - 1),
+// so every row issues the same memory operations.
 template <int J>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, int64_t T,
-                                                   int64_t Hq, int64_t W, int nv, int k,
-                                                   int32_t* __restrict__ out) {
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, const float (&v)[J > 0 ? J : 1],
+                                         int nv, int k, int32_t* __restrict__ dst, uint2* slot,
+                                         int32_t* sel) {
   const int l = lane_id();
-  // grid (ceil(T / 4), Hq): wave w of block (x, h) takes row (h, t = 4x + w)
-  const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (t >= T) return;
-  const int64_t h = blockIdx.y;
-  int32_t* const dst = out + (t * Hq + h) * k;
-  if (nv == 0) {                           // nothing to select; scores may be NULL
-    if (l < k) dst[l] = -1;
-    return;
-  }
-  const float* row = scores + (h * T + t) * W;
   const int nch = (nv + 63) / 64;          // 64-block chunks holding candidates
   const int nj = J > 0 ? J : nch;
-
-  // Every lane loads, at its block index clamped into [0, nv), and blocks
-  // past nv are masked afterwards: the loads carry no branch, so all of a
-  // row's loads are in flight together.
   uint32_t keys[J > 0 ? J : 1];
   if constexpr (J > 0) {
-    float v[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) v[j] = __builtin_nontemporal_load(row + min(j * 64 + l, nv - 1));
 #pragma unroll
     for (int j = 0; j < J; ++j) keys[j] = topk_key(v[j]) & below_mask(j * 64 + l, nv);
   }
@@ -83,12 +81,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 
   // tau = the k-th largest key (0 when the row has at most k candidates), or
   // any lower threshold that exactly k keys reach: the search stops there.
-  // Invariant: at least k keys reach tau, and the bits of tau above `bit`
-  // are final.  Once at most 64 keys reach tau, they are compacted in index
+  // Invariant: at least k keys reach tau, and the bits of tau above the bit mb
+  // under test are final.  Once at most 64 keys reach tau, they are compacted in index
   // order into one register per lane (through a per-wave LDS slot), and the
   // remaining steps and the selection work on that register alone.
-  __shared__ uint2 packed[4][128];
-  uint2* const slot = packed[threadIdx.x >> 6];
   uint32_t tau = 0;
   bool comp = false;
   uint32_t ck = 0;            // compacted key (0 in lanes past the count)
@@ -220,7 +216,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     const uint64_t em = __ballot(eq);
     const bool take = ck > tau || (eq && __popcll(em & below) < need_eq);
     const uint64_t tm = __ballot(take);
-    if (take) dst[__popcll(tm & below)] = ci;
+    if (take) sel[__popcll(tm & below)] = ci;
     taken = __popcll(tm);
   } else {
     const int need_eq = tau == 0 ? 0 : k - count_ge(tau + 1u);
@@ -231,12 +227,65 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       const uint64_t em = __ballot(eq);
       const bool take = kv > tau || (eq && eq_seen + __popcll(em & below) < need_eq);
       const uint64_t tm = __ballot(take);
-      if (take) dst[taken + __popcll(tm & below)] = j * 64 + l;
+      if (take) sel[taken + __popcll(tm & below)] = j * 64 + l;
       taken += __popcll(tm);
       eq_seen += __popcll(em);
     }
   }
-  if (l < k && l >= taken) dst[l] = -1;
+  if (l < k && l >= taken) sel[l] = -1;
+  wave_lds_sync();
+  const int o = min(l, k - 1);
+  dst[o] = sel[o];
+}
+
+// grid (ceil(T / (4 R)), Hq): wave w of block (x, h) takes the rows
+// (h, t) for t = (4 x + w) R + i, i < R; rows past T repeat row T - 1 (same
+// result, same place).  Every lane loads and masks afterwards, so no load
+// carries a branch and a row's loads are all in flight together.
+template <int J, int R>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, int64_t T,
+                                                   int64_t Hq, int64_t W, int nv, int k,
+                                                   int32_t* __restrict__ out) {
+  const int l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t t0 = ((int64_t)blockIdx.x * kTopkWaves + w) * R;
+  if (t0 >= T) return;
+  const int64_t h = blockIdx.y;
+  auto dst_of = [&](int i) { return out + (min(t0 + i, T - 1) * Hq + h) * k; };
+  if (nv == 0) {                           // nothing to select; scores may be NULL
+    for (int i = 0; i < R; ++i)
+      if (l < k) dst_of(i)[l] = -1;
+    return;
+  }
+  __shared__ uint2 packed[kTopkWaves][128];
+  __shared__ int32_t chosen[kTopkWaves][64];
+  auto row_of = [&](int i) { return scores + (h * T + min(t0 + i, T - 1)) * W; };
+  // A row is read through a buffer descriptor (scalar base = the row, size =
+  // nv floats): lane l's load j takes byte offset 4 l + 256 j, the same for
+  // every row, and offsets past the size read as 0 (masked to key 0 later).
+  // The loads skip the caches' usual allocation (nontemporal), being read
+  // once.
+  float v[J > 0 ? J : 1], vn[J > 0 ? J : 1];
+  auto load = [&](float (&d)[J > 0 ? J : 1], const float* row) {
+    if constexpr (J > 0) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(row), 0, 4 * nv, kBufferWord3);
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        d[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * l + 256 * j, 0, kCachePolicyNT));
+    }
+  };
+  load(vn, row_of(0));
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    // the next row's loads stay below the previous row's selection, so at
+    // most two rows' scores are held at a time
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < (J > 0 ? J : 1); ++j) v[j] = vn[j];
+    if (i + 1 < R) load(vn, row_of(i + 1));
+    topk_row<J>(row_of(i), v, nv, k, dst_of(i), packed[w], chosen[w]);
+  }
 }
 
 }  // namespace msa

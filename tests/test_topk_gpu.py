@@ -62,6 +62,15 @@ def test_many_rows_exact(ties, dev):
     assert torch.equal(gpu_topk(s, dev, 512, 16), oracle.block_topk(s, 512, 16))
 
 
+@pytest.mark.parametrize("W,nv,ties", [(100, 100, True), (512, 300, False), (1024, 1024, True)])
+def test_many_rows_ragged_tail(W, nv, ties, dev):
+    # Enough rows that each wave takes several in turn, with T leaving a
+    # partial group of rows at the end of every head.
+    s = synth.score_rows(40 + W, 2, 40003, W, ties=ties)
+    log(f"topk many rows, ragged T: W={W} num_valid={nv} ties={ties}")
+    assert torch.equal(gpu_topk(s, dev, nv, 16), oracle.block_topk(s, nv, 16))
+
+
 def test_degenerate_rows(dev):
     W = 300
     s = torch.full((2, 3, W), float("-inf"))
