@@ -1,6 +1,7 @@
 // Top-k block selection on the score rows, for gfx950.
 //
-// The stage after the block score (the MiniMax-M3 MSA deep-dive, section 4.7
+// The stage after the block score (the notes "MiniMax Sparse Attention:
+// paper algorithm and code", section 4.7
 // "Top-k Block Selection" and section 5.3 "Top-k" with the sparse_topk_select
 // contract; section 6.1 "Exp-free Top-k"): for every (query token t, index
 // head h), the k best blocks of the row score[h, t, 0:num_valid] among those

@@ -147,7 +147,8 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int64_t out_width, void* stream, int32_t family);
 
 /* Top-k block selection on the score rows: the stage the pages place after
- * the block score (the MiniMax-M3 MSA deep-dive, section 4.7 "Top-k Block
+ * the block score (the notes "MiniMax Sparse Attention: paper algorithm and
+ * code", section 4.7 "Top-k Block
  * Selection", section 5.3 "Top-k" with the sparse_topk_select contract,
  * section 6.1 "Exp-free Top-k").
  *

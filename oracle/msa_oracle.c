@@ -332,7 +332,8 @@ int orc_index_score_points(const void* q, int q_dtype, int64_t T, int Hq, int D,
 
 /* ------------------------------------------------------------------------
  * Top-k block selection on the score rows (the follow-on stage the pages
- * describe after the block score: the MiniMax-M3 MSA deep-dive, section 4.7
+ * describe after the block score: the notes "MiniMax Sparse Attention: paper
+ * algorithm and code", section 4.7
  * "Equation (7): Top-k Block Selection" and section 5.3 "Top-k", with the
  * sparse_topk_select contract listed there; section 6.1 "Exp-free Top-k").
  *

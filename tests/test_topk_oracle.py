@@ -1,7 +1,8 @@
 """Pins of the oracle's top-k block selection (CPU only).
 
 The selection follows the follow-on stage the pages describe after the block
-score (the MiniMax-M3 MSA deep-dive, section 4.7 "Top-k Block Selection",
+score (the notes "MiniMax Sparse Attention: paper algorithm and code",
+section 4.7 "Top-k Block Selection",
 section 5.3 "Top-k" with the sparse_topk_select contract, section 6.1
 "Exp-free Top-k"): per (t, h) row, the k best blocks among beta < num_valid
 whose score is above -inf, ties to the lower block index (a reading: the pages
