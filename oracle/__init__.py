@@ -81,7 +81,7 @@ def _bind(lib):
     common = [p, c.c_int, c.c_int64, c.c_int, c.c_int,          # q
               p, c.c_int, c.c_int, c.c_int64, c.c_int, c.c_int,  # k
               p, p, p, c.c_int64, p, p, p, c.c_int,              # strides..B
-              c.c_int, c.c_int, c.c_int]
+              c.c_int, c.c_int, c.c_int, c.c_int]                # modes, counts
     lib.orc_index_score.argtypes = common + [p, c.c_int]
     lib.orc_index_score.restype = c.c_int
     lib.orc_index_score_points.argtypes = common + [p, c.c_int64, p, c.c_int]
@@ -117,7 +117,8 @@ def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 
 def _common(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_len,
-            max_blocks, sparse_mode, init_blocks, local_blocks, block_size=128):
+            max_blocks, sparse_mode, init_blocks, local_blocks, local_mode=0,
+            block_size=128):
     layout = layout.upper()
     assert query.device.type == "cpu" and key.device.type == "cpu"
     q = query.contiguous()
@@ -151,18 +152,21 @@ def _common(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_
     args = [ptr(q), _DT[q.dtype], T, Hq, D,
             ptr(key), _DT[key.dtype], _LAYOUT[layout], key.shape[0], Hkv, P,
             ptr(ks), ptr(sl), ptr(bt), int(max_blocks), ptr(sc), ptr(cu), ptr(kv),
-            int(kv.numel()), int(sparse_mode), int(init_blocks), int(local_blocks)]
+            int(kv.numel()), int(sparse_mode), int(init_blocks), int(local_blocks),
+            int(local_mode)]
     return args, keep, (Hq, T)
 
 
 def index_score(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_len,
-                max_blocks, sparse_mode=3, init_blocks=0, local_blocks=1,
+                max_blocks, sparse_mode=3, init_blocks=0, local_blocks=1, local_mode=0,
                 nthreads: int = 0, lib=None) -> Tuple[torch.Tensor, int]:
-    """Full output ``[Hq, T, RoundUp(MB,16)]`` float32 and the thread count used."""
+    """Full output ``[Hq, T, RoundUp(MB,16)]`` float32 and the thread count used.
+    ``local_mode`` 1 ends the local_mask window at each token's own block
+    (start_loc is then not read)."""
     lib = lib or load()
     args, keep, (Hq, T) = _common(query, key, layout, start_loc, block_table, scale,
                                   cu_seqlens_q, kv_len, max_blocks, sparse_mode,
-                                  init_blocks, local_blocks)
+                                  init_blocks, local_blocks, local_mode)
     W = out_width(max_blocks, lib)
     out = torch.empty((Hq, T, W), dtype=torch.float32)
     rc = lib.orc_index_score(*args, out.data_ptr(), int(nthreads or default_threads()))
@@ -174,12 +178,13 @@ def index_score(query, key, layout, start_loc, block_table, scale, cu_seqlens_q,
 
 def index_score_points(query, key, layout, start_loc, block_table, scale, cu_seqlens_q,
                        kv_len, max_blocks, sparse_mode, init_blocks, local_blocks,
-                       points: torch.Tensor, nthreads: int = 0, lib=None) -> torch.Tensor:
+                       points: torch.Tensor, local_mode=0, nthreads: int = 0,
+                       lib=None) -> torch.Tensor:
     """Entries ``out[h, t, beta]`` for the rows of ``points`` (int64 [n, 3])."""
     lib = lib or load()
     args, keep, _ = _common(query, key, layout, start_loc, block_table, scale,
                             cu_seqlens_q, kv_len, max_blocks, sparse_mode, init_blocks,
-                            local_blocks)
+                            local_blocks, local_mode)
     pts = points.to(torch.int64).contiguous()
     vals = torch.empty(pts.shape[0], dtype=torch.float32)
     rc = lib.orc_index_score_points(*args, pts.data_ptr(), pts.shape[0], vals.data_ptr(),
@@ -197,7 +202,8 @@ def case_args(case) -> dict:
                 start_loc=case.start_loc, block_table=case.block_table, scale=case.scale,
                 cu_seqlens_q=case.cu_seqlens_q, kv_len=case.kv_len,
                 max_blocks=case.max_blocks, sparse_mode=case.sparse_mode,
-                init_blocks=case.init_blocks, local_blocks=case.local_blocks)
+                init_blocks=case.init_blocks, local_blocks=case.local_blocks,
+                local_mode=getattr(case, "local_mode", 0))
 
 
 def index_score_case(case, nthreads: int = 0, lib=None) -> torch.Tensor:

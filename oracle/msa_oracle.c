@@ -30,8 +30,13 @@
  *   After the block max, local_mask (guide, section 二) writes 1e30 on blocks
  *   [0, init_blocks) and then 1e29 on [max(0, start_loc+1-local_blocks),
  *   start_loc], the second overriding the first; it is skipped when both
- *   counts are 0.  Columns past the request's block count, up to the output
- *   width RoundUp(MB, 16), are -inf.
+ *   counts are 0.  With local_mode 1 the window ends instead at the block of
+ *   the token's own position pos = kv_len[b] - L_q(b) + i, floor(pos / P):
+ *   the paper's per-query local block b_local(i) = floor(i / B_k) (notes
+ *   "MiniMax Sparse Attention: paper algorithm and code", section 4.7, on the
+ *   forced local block); start_loc is then not read, and a token before
+ *   position 0 gets no window.  Columns past the request's block count, up to
+ *   the output width RoundUp(MB, 16), are -inf.
  *
  * Arithmetic: every input element is decoded exactly to a double (all input
  * formats embed exactly in binary64); the dot product is summed in binary64 in
@@ -132,6 +137,7 @@ typedef struct {
   const float* scale;            /* int8 keys only */
   const int32_t* cu_q; const int32_t* kv_len; int B;
   int sparse_mode; int init_blocks; int local_blocks;
+  int local_mode;                /* 0: window ends at start_loc[b]; 1: at the token's block */
   int64_t W;                     /* output width */
   int64_t* koff;                 /* [B] packed-key offsets (TND) */
 } orc_args;
@@ -203,10 +209,20 @@ static float entry(const orc_args* a, int h, int64_t t, int64_t beta, double* qr
   }
   float v = (float)best;                         /* one rounding to binary32 */
 
-  /* local_mask, after the max; the local window overrides the init blocks */
+  /* local_mask, after the max; the local window overrides the init blocks.
+   * Its last block is start_loc[b] (per request), or with local_mode 1 the
+   * block holding the token itself, floor(pos / P) at its position
+   * pos = L - Lq + i in the sequence; a token before position 0 has no block
+   * and no window. */
   if (a->init_blocks > 0 || a->local_blocks > 0) {
     if (beta < a->init_blocks) v = 1e30f;
-    int64_t s = a->start_loc[b];
+    int64_t s;
+    if (a->local_mode == 0) {
+      s = a->start_loc[b];
+    } else {
+      int64_t pos = L - Lq + i;
+      s = pos >= 0 ? pos / a->P : -1;
+    }
     int64_t lo = s + 1 - a->local_blocks;
     if (lo < 0) lo = 0;
     if (beta >= lo && beta <= s) v = 1e29f;
@@ -297,7 +313,8 @@ int64_t orc_out_width(int64_t max_blocks) {
   a.start_loc = start_loc; a.block_table = block_table; a.MB = MB;             \
   a.scale = scale; a.cu_q = cu_q; a.kv_len = kv_len; a.B = B;                  \
   a.sparse_mode = sparse_mode; a.init_blocks = init_blocks;                    \
-  a.local_blocks = local_blocks; a.W = orc_out_width(MB);                      \
+  a.local_blocks = local_blocks; a.local_mode = local_mode;                    \
+  a.W = orc_out_width(MB);                                                     \
   a.koff = (int64_t*)calloc(B > 0 ? B : 1, sizeof(int64_t));                   \
   int rc = check(&a);                                                          \
   if (rc) { free(a.koff); return rc; }
@@ -309,7 +326,8 @@ int orc_index_score(const void* q, int q_dtype, int64_t T, int Hq, int D,
                     int P, const int64_t* k_strides, const int32_t* start_loc,
                     const int32_t* block_table, int64_t MB, const float* scale,
                     const int32_t* cu_q, const int32_t* kv_len, int B, int sparse_mode,
-                    int init_blocks, int local_blocks, float* out, int nthreads) {
+                    int init_blocks, int local_blocks, int local_mode, float* out,
+                    int nthreads) {
   ORC_FILL_ARGS
   int used = run(&a, out, NULL, T, nthreads);
   free(a.koff);
@@ -323,7 +341,8 @@ int orc_index_score_points(const void* q, int q_dtype, int64_t T, int Hq, int D,
                            const int32_t* block_table, int64_t MB, const float* scale,
                            const int32_t* cu_q, const int32_t* kv_len, int B,
                            int sparse_mode, int init_blocks, int local_blocks,
-                           const int64_t* pts, int64_t n, float* vals, int nthreads) {
+                           int local_mode, const int64_t* pts, int64_t n, float* vals,
+                           int nthreads) {
   ORC_FILL_ARGS
   int used = run(&a, vals, pts, n, nthreads);
   free(a.koff);

@@ -66,6 +66,7 @@ class MsaCase:
     block_size: int = 128
     gap: int = 0                        # unused pages between used ones (paged)
     poison: Optional[str] = None
+    local_mode: int = 0                 # 0: window at start_loc; 1: at each token's block
 
     @property
     def batch(self) -> int:
@@ -158,7 +159,7 @@ def make_case(name: str, seed: int, *, q_lens: Sequence[int], kv_lens: Sequence[
               table: str = "perm", sparse_mode: int = 3, init_blocks: int = 0,
               local_blocks: int = 1, start_loc: Optional[Sequence[int]] = None,
               kv_len_draw: Optional[tuple] = None, B: Optional[int] = None,
-              extra_pages: int = 0) -> MsaCase:
+              extra_pages: int = 0, local_mode: int = 0) -> MsaCase:
     """Build one case.
 
     ``kv_len_draw=(lo, hi)`` draws ``kv_len`` uniformly in [lo, hi] from the
@@ -167,7 +168,8 @@ def make_case(name: str, seed: int, *, q_lens: Sequence[int], kv_lens: Sequence[
     Paged layouts get ``NP`` pages, by default ``B*MB + extra_pages`` (the
     extra pages are never referenced by a request's visible blocks).
     ``start_loc`` defaults to the block holding each request's first query
-    token, ``max(0, kv_len - q_len) // P``.
+    token, ``max(0, kv_len - q_len) // P``.  ``local_mode`` 1 anchors the
+    local_mask window at each query token's own block instead.
     """
     layout = layout.upper()
     kdtype = kdtype or qdtype
@@ -244,7 +246,7 @@ def make_case(name: str, seed: int, *, q_lens: Sequence[int], kv_lens: Sequence[
         kv_len=torch.from_numpy(kv.astype(np.int32)),
         start_loc=torch.from_numpy(sl.astype(np.int32)),
         max_blocks=int(MB), sparse_mode=sparse_mode, init_blocks=init_blocks,
-        local_blocks=local_blocks, block_size=P, gap=gap)
+        local_blocks=local_blocks, block_size=P, gap=gap, local_mode=local_mode)
 
 
 def config_case(c: int) -> MsaCase:
@@ -438,6 +440,21 @@ def edge_cases() -> List[MsaCase]:
         qdtype="f8e5m2", layout="BBND", extra_pages=4, init_blocks=1, local_blocks=2)
     add("prefill_tnd_f8e5m2", q_lens=[130], kv_lens=[400], Hq=16, Hkv=2, qdtype="f8e5m2",
         layout="TND", init_blocks=1, local_blocks=1)
+    # per-query local window (each token's own block and the ones before it)
+    add("perq_prefill_tnd", q_lens=[300, 77], kv_lens=[556, 77], Hq=16, Hkv=2,
+        qdtype="bf16", layout="TND", init_blocks=1, local_blocks=2, local_mode=1)
+    add("perq_mode0_bbnd", q_lens=[200, 3], kv_lens=[700, 260], Hq=8, Hkv=1, qdtype="f16",
+        layout="BBND", extra_pages=6, sparse_mode=0, local_blocks=3, local_mode=1)
+    add("perq_q_longer_than_kv", q_lens=[10, 4], kv_lens=[6, 130], Hq=4, Hkv=1,
+        qdtype="bf16", layout="BBND", extra_pages=4, init_blocks=1, local_blocks=1,
+        local_mode=1)
+    add("perq_spec_decode_i8", q_lens=[3, 1, 2], kv_lens=[500, 129, 0], Hq=8, Hkv=2,
+        qdtype="f16", kdtype="i8", layout="BNBD", extra_pages=5, local_blocks=2,
+        local_mode=1)
+    add("perq_prefill_bbnd_f8", q_lens=[200], kv_lens=[450], Hq=16, Hkv=2, qdtype="f8e4m3",
+        layout="BBND", extra_pages=6, init_blocks=1, local_blocks=2, local_mode=1)
+    add("perq_prefill_bnbd_wide", q_lens=[260], kv_lens=[1000], Hq=8, Hkv=1, qdtype="bf16",
+        layout="BNBD", MB=40, extra_pages=4, init_blocks=2, local_blocks=4, local_mode=1)
     return cs
 
 
@@ -465,11 +482,13 @@ def random_cases(n: int, seed: int = 4242) -> List[MsaCase]:
         local = int(rng.integers(0, min(3, limit) + 1))
         starts = [int(rng.integers(0, MB if MB is not None else nb)) for _ in range(B)]
         gap = int(rng.choice([0, 0, 1])) if layout != "TND" else 0
+        # drawn from a generator of its own, so the other draws stay as they were
+        local_mode = int(np.random.default_rng(seed + 100000 + i).integers(0, 2))
         out.append(make_case(f"rand{i}_{layout.lower()}_{kd}_g{g}", seed + 1 + i,
                              q_lens=q_lens, kv_lens=kv_lens, Hq=Hkv * g, Hkv=Hkv, qdtype=qd,
                              kdtype=kd, layout=layout, MB=MB, extra_pages=int(rng.integers(0, 4)),
                              gap=gap, sparse_mode=mode, init_blocks=init, local_blocks=local,
-                             start_loc=starts))
+                             start_loc=starts, local_mode=local_mode))
     return out
 
 
@@ -479,6 +498,7 @@ def case_summary(case: MsaCase) -> dict:
         "k": case.key_dtype_name(), "B": case.batch, "T": case.T, "Hq": case.Hq,
         "Hkv": case.Hkv, "MB": case.max_blocks, "mode": case.sparse_mode,
         "init": case.init_blocks, "local": case.local_blocks, "poison": case.poison,
+        "local_mode": case.local_mode,
     }
 
 

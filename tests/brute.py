@@ -4,7 +4,8 @@ It follows the block-selection sketch of the DSA forward-path notes (section
 3, from token scores to block selection): full token scores, ``masked_fill``
 of every invisible position with -inf, ``reshape`` into blocks of P tokens and
 ``amax`` over each block; then the local_mask constants of the msa_index_score
-guide (section 二).  Inputs are decoded with torch's own ``.to(float64)`` and
+guide (section 二), with the window at start_loc or, per query, at each token's
+own block (the paper's local block, MSA notes section 4.7).  Inputs are decoded with torch's own ``.to(float64)`` and
 products are taken with torch matmul, so it shares nothing with the C oracle.
 """
 import torch
@@ -65,8 +66,17 @@ def brute_force(case) -> torch.Tensor:
         out[:, t0:t1, :nb] = blocks
         if case.init_blocks > 0 or case.local_blocks > 0:
             out[:, t0:t1, :case.init_blocks] = 1e30
-            st = int(case.start_loc[b])
-            lo = max(0, st + 1 - case.local_blocks)
-            if st >= lo:
-                out[:, t0:t1, lo:st + 1] = 1e29
+            if getattr(case, "local_mode", 0) == 0:
+                st = int(case.start_loc[b])
+                lo = max(0, st + 1 - case.local_blocks)
+                if st >= lo:
+                    out[:, t0:t1, lo:st + 1] = 1e29
+            else:
+                # each token's own block: the floor of its position over P
+                # (negative before position 0, which leaves no window)
+                anchor = torch.div(L - Lq + torch.arange(Lq), P, rounding_mode="floor")
+                col = torch.arange(W)[None, :]
+                win = (col <= anchor[:, None]) & (col >= anchor[:, None] + 1 - case.local_blocks)
+                out[:, t0:t1, :] = torch.where(win[None], torch.tensor(1e29, dtype=torch.float64),
+                                               out[:, t0:t1, :])
     return out.to(torch.float32)

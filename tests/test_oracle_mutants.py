@@ -38,12 +38,21 @@ MUTANTS = {
     "scale_index_token_major": ("*sidx = (page * a->Hkv + hk) * a->P + jj;",
                                 "*sidx = (page * a->P + jj) * a->Hkv + hk;"),
     "init_after_local": ("    if (beta < a->init_blocks) v = 1e30f;\n", ""),
+    # per-query local window
+    "per_query_ignored": ("if (a->local_mode == 0) {", "if (1) {"),
+    "per_query_block_end": ("s = pos >= 0 ? pos / a->P : -1;",
+                            "s = pos >= 0 ? (pos + 1) / a->P : -1;"),
+    "per_query_from_window_end": ("int64_t pos = L - Lq + i;",
+                                  "int64_t pos = (a->sparse_mode == 3) ? L - Lq + i : L - 1;"),
+    "per_query_negative_to_block0": ("s = pos >= 0 ? pos / a->P : -1;",
+                                     "s = pos >= 0 ? pos / a->P : 0;"),
 }
 
 CASE_NAMES = ["tiny_bbnd_f16", "mix_bbnd_bf16", "mix_bnbd_bf16", "mix_tnd_bf16",
               "mix_bbnd_i8", "mix_bnbd_i8", "mix_tnd_i8", "mix_bbnd_f8e4m3",
               "pad_tnd_kvlen0", "q_longer_than_kv", "init_local_overlap", "mode0_tnd",
-              "gqa_g3_bbnd", "gqa_g40_bbnd", "dim0_gap2_bnbd_i8"]
+              "gqa_g3_bbnd", "gqa_g40_bbnd", "dim0_gap2_bnbd_i8",
+              "perq_prefill_tnd", "perq_mode0_bbnd", "perq_q_longer_than_kv"]
 
 
 @pytest.fixture(scope="module")
