@@ -28,8 +28,10 @@ DTYPE_CODE = {
 LAYOUT_CODE = {"TND": 0, "BBND": 1, "BNBD": 2}
 STATUS_NAMES = ["MSA_OK", "MSA_ERR_NULL", "MSA_ERR_LAYOUT", "MSA_ERR_DTYPE", "MSA_ERR_SHAPE",
                 "MSA_ERR_STRIDE", "MSA_ERR_SCALE", "MSA_ERR_ATTR", "MSA_ERR_HIP"]
-EXPORTED = ("msa_index_score", "msa_index_score_family", "msa_index_score_out_width",
-            "msa_status_str", "msa_index_score_kernel_family", "msa_block_topk")
+EXPORTED = ("msa_index_score", "msa_index_score_family", "msa_index_score_ex",
+            "msa_index_score_out_width", "msa_status_str", "msa_index_score_kernel_family",
+            "msa_block_topk")
+LOCAL_MODE_CODE = {"request": 0, "query": 1}
 
 
 class MsaTensor(ctypes.Structure):
@@ -71,6 +73,9 @@ def load_library(path: Optional[str] = None):
         lib.msa_index_score.restype = ctypes.c_int
         lib.msa_index_score_family.argtypes = args + [ctypes.c_int32]
         lib.msa_index_score_family.restype = ctypes.c_int
+        lib.msa_index_score_ex.argtypes = (args[:13] + [ctypes.c_int32] + args[13:] +
+                                           [ctypes.c_int32])
+        lib.msa_index_score_ex.restype = ctypes.c_int
         lib.msa_index_score_out_width.argtypes = [ctypes.c_int64]
         lib.msa_index_score_out_width.restype = ctypes.c_int64
         lib.msa_status_str.argtypes = [ctypes.c_int32]
@@ -125,9 +130,12 @@ def msa_index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Ten
                     block_table: Optional[torch.Tensor], scale: Optional[torch.Tensor],
                     cu_seqlens_q: torch.Tensor, kv_len: torch.Tensor, layout,
                     sparse_mode: int, init_blocks: int, local_blocks: int, out: torch.Tensor,
-                    max_blocks: int, stream=None, family: int = -1) -> torch.Tensor:
+                    max_blocks: int, stream=None, family: int = -1,
+                    local_mode=0) -> torch.Tensor:
     """Call the C ABI on device tensors; ``out`` ([Hq, T, W] float32) is filled
-    asynchronously on ``stream`` (default: torch's current stream)."""
+    asynchronously on ``stream`` (default: torch's current stream).
+    ``local_mode`` 0/"request" ends the local window at start_loc, 1/"query"
+    at each token's own block (start_loc may then be None)."""
     lib = load_library()
     dev = out.device
     for name, t in (("query", query), ("key", key), ("start_loc", start_loc),
@@ -152,7 +160,10 @@ def msa_index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Ten
             int(max_blocks), _ptr(scale), _ptr(cu_seqlens_q), _ptr(kv_len),
             int(kv_len.numel()), _layout_code(layout), int(sparse_mode), int(init_blocks),
             int(local_blocks), _ptr(out), int(out.shape[2]), ctypes.c_void_p(stream))
-    if family == -1:
+    lm = LOCAL_MODE_CODE.get(local_mode, -1) if isinstance(local_mode, str) else int(local_mode)
+    if lm != 0:
+        st = lib.msa_index_score_ex(*args[:13], lm, *args[13:], int(family))
+    elif family == -1:
         st = lib.msa_index_score(*args)
     else:
         st = lib.msa_index_score_family(*args, int(family))
@@ -167,7 +178,8 @@ def index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Tensor,
                 actual_seq_qlen: Optional[torch.Tensor] = None,
                 actual_seq_klen: Optional[torch.Tensor] = None, layout_key: str = "BBND",
                 sparse_mode: int = 3, init_blocks: int = 0, local_blocks: int = 1,
-                max_blocks: Optional[int] = None, stream=None, family: int = -1) -> torch.Tensor:
+                max_blocks: Optional[int] = None, stream=None, family: int = -1,
+                local_mode=0) -> torch.Tensor:
     """Allocate ``[Hq, T, RoundUp(MB, 16)]`` float32 and fill it.
 
     ``actual_seq_qlen`` is the ``[B+1]`` query prefix sum, ``actual_seq_klen``
@@ -189,7 +201,7 @@ def index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Tensor,
                       device=query.device)
     return msa_index_score(query, key, start_loc, block_table, scale, actual_seq_qlen,
                            actual_seq_klen, lay, sparse_mode, init_blocks, local_blocks, out,
-                           max_blocks, stream=stream, family=family)
+                           max_blocks, stream=stream, family=family, local_mode=local_mode)
 
 
 def msa_block_topk(scores: torch.Tensor, num_valid: int, k: int, out: torch.Tensor,

@@ -49,6 +49,7 @@ struct Params {
   int32_t MB, W;
   int32_t paged, causal;
   int32_t init_blocks, local_blocks;
+  int32_t local_per_query;     // 1: the local window ends at each token's own block
   int32_t hpt;                 // heads of a KV group per tile
   int32_t tpt;                 // query tokens per tile
   int32_t hchunks;             // ceil(g / hpt)
@@ -230,6 +231,17 @@ __device__ __forceinline__ int last_visible(const Params& p, const Work& w, int 
 // msa_index_score, section 二: 1e30 on [0, init_blocks), then 1e29 on
 // [max(0, start_loc+1-local_blocks), start_loc], skipped when both are 0;
 // requests with kv_len = 0 are skipped whole, section 四).
+// Last block of the local_mask window for token i of the work item's request:
+// start_loc[b], or (per query) the block of the token's own position
+// L - Lq + i, -1 (no window) before position 0 -- the paper's per-query local
+// block (notes "MiniMax Sparse Attention: paper algorithm and code", section
+// 4.7, forced local block).
+__device__ __forceinline__ int local_anchor(const Params& p, const Work& w, int i) {
+  if (!p.local_per_query) return p.start_loc[w.b];
+  const int pos = w.L - w.Lq + i;
+  return pos >= 0 ? pos / kP : -1;
+}
+
 __device__ __forceinline__ float finish(const Params& p, int L, int start, int beta,
                                         bool scored, float v) {
   float r = scored ? v : -__builtin_inff();

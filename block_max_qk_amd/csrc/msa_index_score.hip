@@ -81,12 +81,14 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
                  const int32_t* block_table, int64_t max_blocks, const float* scale,
                  const int32_t* cu_seqlens_q, const int32_t* kv_len, int32_t batch,
                  int32_t layout, int32_t sparse_mode, int32_t init_blocks,
-                 int32_t local_blocks, float* out, int64_t out_width, void* stream,
-                 int32_t family) {
+                 int32_t local_blocks, int32_t local_mode, float* out, int64_t out_width,
+                 void* stream, int32_t family) {
   // Pointers that a call with no requests (B = 0) or no query tokens (T = 0)
   // never reads may be NULL there; torch hands empty tensors a NULL address.
+  // start_loc is not read with the per-query local window.
   if (!query || !key || !cu_seqlens_q) return MSA_ERR_NULL;
-  if (batch > 0 && (!kv_len || !start_loc)) return MSA_ERR_NULL;
+  if (batch > 0 && (!kv_len || (!start_loc && local_mode != MSA_LOCAL_PER_QUERY)))
+    return MSA_ERR_NULL;
   if (query->ndim == 3 && query->shape[0] > 0 && !out) return MSA_ERR_NULL;
   if (layout != MSA_LAYOUT_TND && layout != MSA_LAYOUT_BBND && layout != MSA_LAYOUT_BNBD)
     return MSA_ERR_LAYOUT;
@@ -179,6 +181,8 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (init_blocks < 0 || local_blocks < 0 || init_blocks > limit || local_blocks > limit)
     return MSA_ERR_ATTR;
   if (family < -1 || family > 1) return MSA_ERR_ATTR;
+  if (local_mode != MSA_LOCAL_PER_REQUEST && local_mode != MSA_LOCAL_PER_QUERY)
+    return MSA_ERR_ATTR;
 
   // sizes the kernels index with 32-bit integers
   if (W > (1 << 24) || Hq > (1 << 16) || batch > (1 << 30) || T > (int64_t(1) << 31) - 1 ||
@@ -226,6 +230,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.causal = sparse_mode == 3 ? 1 : 0;
   p.init_blocks = init_blocks;
   p.local_blocks = local_blocks;
+  p.local_per_query = local_mode == MSA_LOCAL_PER_QUERY ? 1 : 0;
   p.hpt = std::min<int32_t>(g, rows);
   p.tpt = rows / p.hpt;
   p.hchunks = (g + p.hpt - 1) / p.hpt;
@@ -268,7 +273,8 @@ msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
                              int32_t init_blocks, int32_t local_blocks, float* out,
                              int64_t out_width, void* stream) {
   return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
-             layout, sparse_mode, init_blocks, local_blocks, out, out_width, stream, -1);
+             layout, sparse_mode, init_blocks, local_blocks, MSA_LOCAL_PER_REQUEST, out,
+             out_width, stream, -1);
 }
 
 msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_t* key,
@@ -279,7 +285,20 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int32_t init_blocks, int32_t local_blocks, float* out,
                                     int64_t out_width, void* stream, int32_t family) {
   return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
-             layout, sparse_mode, init_blocks, local_blocks, out, out_width, stream, family);
+             layout, sparse_mode, init_blocks, local_blocks, MSA_LOCAL_PER_REQUEST, out,
+             out_width, stream, family);
+}
+
+msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* key,
+                                const int32_t* start_loc, const int32_t* block_table,
+                                int64_t max_blocks, const float* scale,
+                                const int32_t* cu_seqlens_q, const int32_t* kv_len,
+                                int32_t batch, int32_t layout, int32_t sparse_mode,
+                                int32_t init_blocks, int32_t local_blocks, int32_t local_mode,
+                                float* out, int64_t out_width, void* stream, int32_t family) {
+  return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
+             layout, sparse_mode, init_blocks, local_blocks, local_mode, out, out_width, stream,
+             family);
 }
 
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,

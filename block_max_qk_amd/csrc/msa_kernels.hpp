@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
       const int rh = hc * p.hpt + (r - ri * p.hpt);
       if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
       float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
-      const int start = p.start_loc[w.b];
+      const int start = local_anchor(p, w, c.j * p.tpt + ri);
       const int v0 = c.nvis;
       const int a0 = min((v0 + 3) & ~3, p.W);
       if ((int)threadIdx.x < a0 - v0)
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
       row_ok = (n < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
       lim = row_ok ? last_visible(p, w, i0 + ti) : -1;
       lim_lo = last_visible(p, w, i0);
-      start = p.start_loc[w.b];
+      start = local_anchor(p, w, i0 + ti);
 #pragma unroll
       for (int s = 0; s < 4; ++s) qv[s] = i32x4{0, 0, 0, 0};
       if (row_ok) {
@@ -633,6 +633,7 @@ void prefill_kernel(Params p) {
   constexpr int NOUT = (NTW + 1) / 2;
   bool orow_ok[NOUT];
   float* orow_ptr[NOUT];
+  int oanc[NOUT];               // last block of each output row's local window
 #pragma unroll
   for (int u = 0; u < NOUT; ++u) {
     const int orow = wave * 32 * NTW + (G + 2 * u) * 32 + n;
@@ -640,8 +641,8 @@ void prefill_kernel(Params p) {
     const int ohg = w.hc * p.hpt + (orow - oti * p.hpt);
     orow_ok[u] = G + 2 * u < NTW && orow < p.hpt * p.tpt && oti < w.ntok && ohg < p.g;
     orow_ptr[u] = p.out + (((int64_t)w.hk * p.g + ohg) * p.T + (w.t0 + oti)) * p.W;
+    oanc[u] = local_anchor(p, w, i0 + oti);
   }
-  const int ostart = p.start_loc[w.b];
 
   const int nst = busy ? (vend - w.c0) * SPB : 0;   // stages of this work item
   if constexpr (ASYNC) {
@@ -681,7 +682,7 @@ void prefill_kernel(Params p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int beta = g0 + c + e;
-              v[e] = finish(p, w.L, ostart, beta, beta < vend, resv[u][c + e]);
+              v[e] = finish(p, w.L, oanc[u], beta, beta < vend, resv[u][c + e]);
             }
             *reinterpret_cast<f32x4*>(orow_ptr[u] + g0 + c) = v;
           }
@@ -840,7 +841,7 @@ void prefill_kernel(Params p) {
       for (int beta = done; beta < w.c1; beta += 4) {
         f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, ostart, beta + e, false, 0.f);
+        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, oanc[u], beta + e, false, 0.f);
         *reinterpret_cast<f32x4*>(orow_ptr[u] + beta) = v;
       }
     }

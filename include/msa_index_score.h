@@ -46,13 +46,23 @@ typedef enum {
   MSA_ERR_SHAPE = 4,   /* shapes disagree with each other or with the layout */
   MSA_ERR_STRIDE = 5,  /* a key axis other than dim0 is not compact (guide, 8.1) */
   MSA_ERR_SCALE = 6,   /* int8 key without scale, or scale with a non-int8 key */
-  MSA_ERR_ATTR = 7,    /* sparse_mode not 0/3, or init/local_blocks out of range */
+  MSA_ERR_ATTR = 7,    /* sparse_mode not 0/3, init/local_blocks out of range, or
+                          another attribute (family, local_mode, top-k k) invalid */
   MSA_ERR_HIP = 8      /* a HIP runtime call or kernel launch failed */
 } msa_status_t;
 
 /* Key layouts (guide, section 四): packed [T2, Hkv, D]; paged
  * [NP, P, Hkv, D] (BBND) and [NP, Hkv, P, D] (BNBD). */
 typedef enum { MSA_LAYOUT_TND = 0, MSA_LAYOUT_BBND = 1, MSA_LAYOUT_BNBD = 2 } msa_layout_t;
+
+/* Where local_mask's window of local_blocks blocks ends.  PER_REQUEST: at
+ * start_loc[b] for every token of request b (guide, section 二).  PER_QUERY:
+ * at each query token's own block, floor(pos / 128) with pos = kv_len[b] -
+ * L_q(b) + i the token's position in the sequence -- the paper's forced local
+ * block b_local(i) (notes "MiniMax Sparse Attention: paper algorithm and
+ * code", section 4.7, which observes that a request-wide window is not the
+ * same in a long prefill).  A token before position 0 gets no window. */
+typedef enum { MSA_LOCAL_PER_REQUEST = 0, MSA_LOCAL_PER_QUERY = 1 } msa_local_mode_t;
 
 /* Element types.  Supported (query, key) pairs: (F16, F16), (BF16, BF16),
  * (F16, I8) with a float32 scale, (F8E4M3, F8E4M3) and (F8E5M2, F8E5M2)
@@ -145,6 +155,20 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int32_t batch, int32_t layout, int32_t sparse_mode,
                                     int32_t init_blocks, int32_t local_blocks, float* out,
                                     int64_t out_width, void* stream, int32_t family);
+
+/* Same as msa_index_score_family, with the local_mask window's placement
+ * chosen by local_mode (msa_local_mode_t; any other value returns
+ * MSA_ERR_ATTR).  With MSA_LOCAL_PER_QUERY start_loc is not read and may be
+ * NULL; everything else (arguments, ownership, errors) is as for
+ * msa_index_score.  msa_index_score is this call with MSA_LOCAL_PER_REQUEST
+ * and family -1. */
+msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* key,
+                                const int32_t* start_loc, const int32_t* block_table,
+                                int64_t max_blocks, const float* scale,
+                                const int32_t* cu_seqlens_q, const int32_t* kv_len,
+                                int32_t batch, int32_t layout, int32_t sparse_mode,
+                                int32_t init_blocks, int32_t local_blocks, int32_t local_mode,
+                                float* out, int64_t out_width, void* stream, int32_t family);
 
 /* Top-k block selection on the score rows: the stage the pages place after
  * the block score (the notes "MiniMax Sparse Attention: paper algorithm and

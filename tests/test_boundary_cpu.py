@@ -80,13 +80,16 @@ def tdesc(shape, stride=None, dtype=0, addr=FAKE):
 
 
 def call(q=None, k=None, *, start=FAKE, table=FAKE, mb=2, scale=None, cu=FAKE, kv=FAKE, B=1,
-         layout=1, mode=3, init=0, local=1, out=FAKE, width=16, family=None):
+         layout=1, mode=3, init=0, local=1, out=FAKE, width=16, family=None, local_mode=None):
     lib = m.load_library()
     q = q if q is not None else tdesc([32, 8, 128], dtype=DT["f16"])
     k = k if k is not None else tdesc([8, 128, 1, 128], dtype=DT["f16"])
     args = [ctypes.byref(q) if q is not False else None,
             ctypes.byref(k) if k is not False else None,
             start, table, mb, scale, cu, kv, B, layout, mode, init, local, out, width, None]
+    if local_mode is not None:
+        return lib.msa_index_score_ex(*args[:13], local_mode, *args[13:],
+                                      -1 if family is None else family)
     if family is None:
         return lib.msa_index_score(*args)
     return lib.msa_index_score_family(*args, family)
@@ -203,6 +206,22 @@ def test_attribute_rules():
     assert call(q=q0, k=tnd, layout=0, table=None, mb=3, init=17) == ATTR
     assert call(family=2) == ATTR
     assert call(family=-2) == ATTR
+
+
+def test_local_mode_rules():
+    q0 = tdesc([0, 8, 128], dtype=0)
+    assert call(local_mode=2) == ATTR
+    assert call(local_mode=-1) == ATTR
+    assert call(q=q0, local_mode=0) == OK
+    assert call(q=q0, local_mode=1) == OK
+    # start_loc is needed for the per-request window only
+    assert call(start=None, local_mode=0) == NULL
+    assert call(q=q0, start=None, local_mode=1) == OK
+    assert call(start=None, local_mode=1, family=5) == ATTR   # validation goes on past it
+    # the other checks are the same as msa_index_score's
+    assert call(mode=1, local_mode=1) == ATTR
+    assert call(width=32, local_mode=1) == SHAPE
+    assert call(cu=None, local_mode=1) == NULL
 
 
 def test_block_topk_validation_without_launch():

@@ -56,7 +56,8 @@ def run_gpu(case, dev, family=-1):
     out = torch.full((case.Hq, case.T, W), 12345.0, dtype=torch.float32, device=dev)
     m.msa_index_score(d["query"], d["key"], d["start_loc"], d["block_table"], d["scale"],
                       d["cu_seqlens_q"], d["kv_len"], case.layout, case.sparse_mode,
-                      case.init_blocks, case.local_blocks, out, case.max_blocks, family=family)
+                      case.init_blocks, case.local_blocks, out, case.max_blocks, family=family,
+                      local_mode=case.local_mode)
     torch.cuda.synchronize()
     return out.cpu()
 
@@ -160,3 +161,30 @@ def test_full_size_config_parity(c_idx, dev):
     assert r["ok"], r
     r2 = compare_values(ref[nfull:], gv[nfull:], tol_of(c))
     assert r2["ok"], r2
+
+
+@pytest.mark.parametrize("c_idx", [2, 4])
+def test_full_size_per_query_local_window(c_idx, dev):
+    # The prefill workloads with the local window at each token's own block:
+    # sampled rows and entries against the oracle, and on every row of the
+    # output the token's own block carries the forced 1e29.
+    import dataclasses
+    c = dataclasses.replace(synth.config_case(c_idx), local_mode=1)
+    log(f"[gpu] config {c.name}, per-query local window")
+    got = run_gpu(c, dev)
+    pts, nrows = _sample_points(c, got.shape, 32, 10000, 199 + c_idx)
+    ref = oracle.index_score_case_points(c, pts)
+    gv = got[pts[:, 0], pts[:, 1], pts[:, 2]]
+    W = got.shape[2]
+    nfull = nrows * W
+    r = check(ref[:nfull].reshape(nrows, W), gv[:nfull].reshape(nrows, W), tol_of(c))
+    log(f"[gpu] {c.name} per-query sampled rows: {r}")
+    assert r["ok"], r
+    r2 = compare_values(ref[nfull:], gv[nfull:], tol_of(c))
+    assert r2["ok"], r2
+    cu, kv = c.cu_seqlens_q.long(), c.kv_len.long()
+    for b in range(c.batch):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        pos = int(kv[b]) - (t1 - t0) + torch.arange(t1 - t0)
+        own = got[:, t0:t1].gather(2, (pos // 128).clamp(min=0)[None, :, None].expand(c.Hq, -1, 1))
+        assert bool((own[:, pos >= 0] == 1e29).all()), c.name
