@@ -17,7 +17,8 @@ Output: one JSON line (rank 0 of 1).  ``--config all`` prints one line per
 workload instead (for measurement; the default line is the headline).
 ``--topk`` times the top-k block selection (msa_block_topk, k = 16) over the
 chosen workload's score rows instead, with its own roofline (HBM bytes: every
-row's num_valid scores read, its k indices written).
+row's num_valid scores read, its k indices written).  ``--local-mode query``
+runs the workload with the local_mask window at each token's own block.
 """
 from __future__ import annotations
 
@@ -88,7 +89,8 @@ def workload_stats(case) -> dict:
 
 
 def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
-                 cpu_baseline: bool, args) -> dict:
+                 cpu_baseline: bool, args, local_mode: int = 0) -> dict:
+    import dataclasses
     import torch
     import block_max_qk_amd as m
     from block_max_qk_amd._binding import describe
@@ -98,6 +100,8 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     dev = torch.device("cuda:0")
     t_gen = time.time()
     case = synth.config_case(c_idx)
+    if local_mode:
+        case = dataclasses.replace(case, local_mode=local_mode)
     t_gen = time.time() - t_gen
     stats = workload_stats(case)
     kname = case.key_dtype_name()
@@ -131,10 +135,10 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
              None if scales[i] is None else ctypes.c_void_p(scales[i].data_ptr()),
              ctypes.c_void_p(cu.data_ptr()), ctypes.c_void_p(kv.data_ptr()), case.batch,
              m._binding.LAYOUT_CODE[case.layout], case.sparse_mode, case.init_blocks,
-             case.local_blocks, ctypes.c_void_p(out.data_ptr()), W,
+             case.local_blocks, case.local_mode, ctypes.c_void_p(out.data_ptr()), W,
              ctypes.c_void_p(stream.cuda_stream), family)
         calls.append(a)
-    fn = lib.msa_index_score_family
+    fn = lib.msa_index_score_ex
 
     def step(i):
         st = fn(*calls[i % copies])
@@ -168,7 +172,8 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
         pk = PEAK_TFLOPS[kname]
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": pk, "unit": "TFLOP/s",
                 "frac": round(tflops / pk, 4)}
-    roof["traffic"] = measured_traffic(case.name)
+    # counters were taken with the per-request window (same memory accesses)
+    roof["traffic"] = measured_traffic(case.name) if case.local_mode == 0 else None
     roof["kernel"] = ("decode_kernel" if is_decode else "prefill_kernel") + f"<{kname}>"
     roof["kernel_ms_avg"] = round(kernel_ms, 5)
     roof["gpu_ms_per_step_span"] = round(span_ms, 5)
@@ -187,6 +192,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                    "layout": case.layout, "query_dtype": case.query_dtype_name(),
                    "key_dtype": kname, "sparse_mode": case.sparse_mode,
                    "init_blocks": case.init_blocks, "local_blocks": case.local_blocks,
+                   "local_window": "per-query" if case.local_mode else "per-request",
                    "key_cache_copies": copies, "kernel_family": "decode" if is_decode
                    else "prefill"},
         "hbm_gbs": round(gbs, 1), "mfma_tflops": round(tflops, 3),
@@ -337,6 +343,9 @@ def main():
     ap.add_argument("--topk", action="store_true",
                     help="time the top-k block selection on the workload's scores instead")
     ap.add_argument("--cpu-topk-rows", type=int, default=200000)
+    ap.add_argument("--local-mode", choices=["request", "query"], default="request",
+                    help="local_mask window at start_loc (the workloads' own setting) or at "
+                         "each token's own block")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the operator, run this many MiB device copies "
                          "(counter calibration)")
@@ -382,7 +391,8 @@ def main():
         if copies <= 0:
             copies = 4 if c in (1, 3) else 1
         r = bench_config(c, args.steps, args.warmup, copies, args.family,
-                         not args.no_cpu_baseline, args)
+                         not args.no_cpu_baseline, args,
+                         local_mode=1 if args.local_mode == "query" else 0)
         print(json.dumps(r), flush=True)
 
 
