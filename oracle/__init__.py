@@ -38,6 +38,7 @@ _DT = {
     torch.int8: 2,
     torch.float8_e4m3fn: 3,
     torch.float8_e5m2: 4,
+    torch.uint8: 5,          # MXFP4: E2M1 values packed two per byte, low nibble first
 }
 _LAYOUT = {"TND": 0, "BBND": 1, "BNBD": 2}
 
@@ -80,7 +81,7 @@ def _bind(lib):
     p = c.c_void_p
     common = [p, c.c_int, c.c_int64, c.c_int, c.c_int,          # q
               p, c.c_int, c.c_int, c.c_int64, c.c_int, c.c_int,  # k
-              p, p, p, c.c_int64, p, p, p, c.c_int,              # strides..B
+              p, p, p, c.c_int64, p, p, p, p, p, c.c_int,        # strides..B
               c.c_int, c.c_int, c.c_int, c.c_int]                # modes, counts
     lib.orc_index_score.argtypes = common + [p, c.c_int]
     lib.orc_index_score.restype = c.c_int
@@ -88,6 +89,10 @@ def _bind(lib):
     lib.orc_index_score_points.restype = c.c_int
     lib.orc_out_width.argtypes = [c.c_int64]
     lib.orc_out_width.restype = c.c_int64
+    lib.orc_decode_e2m1.argtypes = [c.c_uint8]
+    lib.orc_decode_e2m1.restype = c.c_double
+    lib.orc_decode_e8m0.argtypes = [c.c_uint8]
+    lib.orc_decode_e8m0.restype = c.c_double
     lib.orc_decode_buffer.argtypes = [p, c.c_int, c.c_int64, p]
     lib.orc_decode_buffer.restype = None
     lib.orc_block_topk.argtypes = [p, c.c_int64, c.c_int64, c.c_int64, c.c_int64, c.c_int, p]
@@ -101,11 +106,13 @@ def out_width(max_blocks: int, lib=None) -> int:
 
 def decode(buf: torch.Tensor, lib=None) -> np.ndarray:
     """Decode every element of a CPU tensor to float64 with the oracle's own
-    decoders."""
+    decoders (uint8 holds packed MXFP4 pairs: two elements per byte, without
+    their group scales)."""
     buf = buf.contiguous()
-    out = np.empty(buf.numel(), dtype=np.float64)
+    n = buf.numel() * (2 if buf.dtype == torch.uint8 else 1)
+    out = np.empty(n, dtype=np.float64)
     (lib or load()).orc_decode_buffer(ctypes.c_void_p(buf.data_ptr()), _DT[buf.dtype],
-                                      buf.numel(), out.ctypes.data)
+                                      n, out.ctypes.data)
     return out
 
 
@@ -118,11 +125,14 @@ def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 def _common(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_len,
             max_blocks, sparse_mode, init_blocks, local_blocks, local_mode=0,
-            block_size=128):
+            q_mx_scale=None, k_mx_scale=None, block_size=128):
     layout = layout.upper()
     assert query.device.type == "cpu" and key.device.type == "cpu"
     q = query.contiguous()
     T, Hq, D = q.shape
+    mx = q.dtype == torch.uint8           # MXFP4: the last axis holds 2 elements per byte
+    if mx:
+        D *= 2
     if layout == "TND":
         Hkv, P = key.shape[1], int(block_size)
         strides = list(key.stride()) + [0]
@@ -134,13 +144,19 @@ def _common(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_
         strides = list(key.stride())
     else:
         raise ValueError(layout)
+    if mx:
+        # element strides of the packed key: outer axes in bytes * 2, D axis 1
+        strides = [2 * x for x in strides[:-1]] + [1] if layout != "TND" else \
+            [2 * strides[0], 2 * strides[1], 1, 0]
     ks = np.asarray(strides, dtype=np.int64)
     sl = _i32(start_loc)
     bt = _i32(block_table)
     cu = _i32(cu_seqlens_q)
     kv = _i32(kv_len)
     sc = scale.to(torch.float32).contiguous() if scale is not None else None
-    keep = (q, key, ks, sl, bt, cu, kv, sc)
+    qmx = q_mx_scale.contiguous() if q_mx_scale is not None else None
+    kmx = k_mx_scale.contiguous() if k_mx_scale is not None else None
+    keep = (q, key, ks, sl, bt, cu, kv, sc, qmx, kmx)
 
     def ptr(t):
         if t is None:
@@ -151,7 +167,8 @@ def _common(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_
 
     args = [ptr(q), _DT[q.dtype], T, Hq, D,
             ptr(key), _DT[key.dtype], _LAYOUT[layout], key.shape[0], Hkv, P,
-            ptr(ks), ptr(sl), ptr(bt), int(max_blocks), ptr(sc), ptr(cu), ptr(kv),
+            ptr(ks), ptr(sl), ptr(bt), int(max_blocks), ptr(sc), ptr(qmx), ptr(kmx),
+            ptr(cu), ptr(kv),
             int(kv.numel()), int(sparse_mode), int(init_blocks), int(local_blocks),
             int(local_mode)]
     return args, keep, (Hq, T)
@@ -159,6 +176,7 @@ def _common(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_
 
 def index_score(query, key, layout, start_loc, block_table, scale, cu_seqlens_q, kv_len,
                 max_blocks, sparse_mode=3, init_blocks=0, local_blocks=1, local_mode=0,
+                q_mx_scale=None, k_mx_scale=None,
                 nthreads: int = 0, lib=None) -> Tuple[torch.Tensor, int]:
     """Full output ``[Hq, T, RoundUp(MB,16)]`` float32 and the thread count used.
     ``local_mode`` 1 ends the local_mask window at each token's own block
@@ -166,7 +184,8 @@ def index_score(query, key, layout, start_loc, block_table, scale, cu_seqlens_q,
     lib = lib or load()
     args, keep, (Hq, T) = _common(query, key, layout, start_loc, block_table, scale,
                                   cu_seqlens_q, kv_len, max_blocks, sparse_mode,
-                                  init_blocks, local_blocks, local_mode)
+                                  init_blocks, local_blocks, local_mode, q_mx_scale,
+                                  k_mx_scale)
     W = out_width(max_blocks, lib)
     out = torch.empty((Hq, T, W), dtype=torch.float32)
     rc = lib.orc_index_score(*args, out.data_ptr(), int(nthreads or default_threads()))
@@ -178,13 +197,13 @@ def index_score(query, key, layout, start_loc, block_table, scale, cu_seqlens_q,
 
 def index_score_points(query, key, layout, start_loc, block_table, scale, cu_seqlens_q,
                        kv_len, max_blocks, sparse_mode, init_blocks, local_blocks,
-                       points: torch.Tensor, local_mode=0, nthreads: int = 0,
-                       lib=None) -> torch.Tensor:
+                       points: torch.Tensor, local_mode=0, q_mx_scale=None,
+                       k_mx_scale=None, nthreads: int = 0, lib=None) -> torch.Tensor:
     """Entries ``out[h, t, beta]`` for the rows of ``points`` (int64 [n, 3])."""
     lib = lib or load()
     args, keep, _ = _common(query, key, layout, start_loc, block_table, scale,
                             cu_seqlens_q, kv_len, max_blocks, sparse_mode, init_blocks,
-                            local_blocks, local_mode)
+                            local_blocks, local_mode, q_mx_scale, k_mx_scale)
     pts = points.to(torch.int64).contiguous()
     vals = torch.empty(pts.shape[0], dtype=torch.float32)
     rc = lib.orc_index_score_points(*args, pts.data_ptr(), pts.shape[0], vals.data_ptr(),
@@ -203,7 +222,9 @@ def case_args(case) -> dict:
                 cu_seqlens_q=case.cu_seqlens_q, kv_len=case.kv_len,
                 max_blocks=case.max_blocks, sparse_mode=case.sparse_mode,
                 init_blocks=case.init_blocks, local_blocks=case.local_blocks,
-                local_mode=getattr(case, "local_mode", 0))
+                local_mode=getattr(case, "local_mode", 0),
+                q_mx_scale=getattr(case, "q_mx_scale", None),
+                k_mx_scale=getattr(case, "k_mx_scale", None))
 
 
 def index_score_case(case, nthreads: int = 0, lib=None) -> torch.Tensor:

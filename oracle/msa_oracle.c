@@ -53,7 +53,7 @@
 #include <unistd.h>
 
 /* element type codes accepted by this oracle */
-enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_F8E4M3 = 3, ORC_F8E5M2 = 4 };
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_I8 = 2, ORC_F8E4M3 = 3, ORC_F8E5M2 = 4, ORC_MXFP4 = 5 };
 /* key layouts */
 enum { ORC_TND = 0, ORC_BBND = 1, ORC_BNBD = 2 };
 
@@ -112,6 +112,19 @@ double orc_decode_e5m2(uint8_t x) {
   return s ? -v : v;
 }
 
+/* OCP microscaling FP4 element, E2M1: sign, 2-bit exponent (bias 1), 1-bit
+ * fraction; exponent 0 is subnormal (0 or 0.5); no infinities or NaNs;
+ * largest 6. */
+double orc_decode_e2m1(uint8_t x) {
+  int s = (x >> 3) & 1, e = (x >> 1) & 3, f = x & 1;
+  double v = e == 0 ? 0.5 * f : ldexp((double)(2 + f), e - 2);   /* (1 + f/2) * 2^(e-1) */
+  return s ? -v : v;
+}
+
+/* OCP microscaling shared scale, E8M0: an unsigned power-of-two exponent,
+ * 2^(e - 127); e = 255 is NaN. */
+double orc_decode_e8m0(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
 static double elem(const void* base, int dtype, int64_t i) {
   switch (dtype) {
     case ORC_F16: return orc_decode_f16(((const uint16_t*)base)[i]);
@@ -119,6 +132,9 @@ static double elem(const void* base, int dtype, int64_t i) {
     case ORC_I8: return (double)((const int8_t*)base)[i];
     case ORC_F8E4M3: return orc_decode_e4m3fn(((const uint8_t*)base)[i]);
     case ORC_F8E5M2: return orc_decode_e5m2(((const uint8_t*)base)[i]);
+    /* MXFP4 values: two per byte, element 2k in the low nibble (the group
+     * scale is applied by the caller) */
+    case ORC_MXFP4: return orc_decode_e2m1((((const uint8_t*)base)[i >> 1] >> (4 * (i & 1))) & 15);
     default: return NAN;
   }
 }
@@ -135,6 +151,8 @@ typedef struct {
   const int32_t* start_loc;
   const int32_t* block_table; int64_t MB;
   const float* scale;            /* int8 keys only */
+  const uint8_t* q_mx;           /* MXFP4: E8M0 scale per 32 query elements [T, Hq, D/32] */
+  const uint8_t* k_mx;           /* MXFP4: the same for keys, the key's layout with D/32 */
   const int32_t* cu_q; const int32_t* kv_len; int B;
   int sparse_mode; int init_blocks; int local_blocks;
   int local_mode;                /* 0: window ends at start_loc[b]; 1: at the token's block */
@@ -170,6 +188,17 @@ static void key_row(const orc_args* a, int b, int64_t j, int hk, int64_t* off,
   }
 }
 
+/* Index of the first MXFP4 scale of key row j of request b, head hk: the
+ * scales form a compact tensor in the key's layout with D/32 per row. */
+static int64_t mx_key_row(const orc_args* a, int b, int64_t j, int hk) {
+  int64_t groups = a->D / 32;
+  if (a->layout == ORC_TND) return ((a->koff[b] + j) * a->Hkv + hk) * groups;
+  int64_t page = a->block_table[(int64_t)b * a->MB + j / a->P];
+  int64_t jj = j % a->P;
+  if (a->layout == ORC_BBND) return ((page * a->P + jj) * a->Hkv + hk) * groups;
+  return ((page * a->Hkv + hk) * a->P + jj) * groups;
+}
+
 static int64_t d_stride(const orc_args* a) {
   return a->layout == ORC_TND ? a->ks[2] : a->ks[3];
 }
@@ -194,14 +223,22 @@ static float entry(const orc_args* a, int h, int64_t t, int64_t beta, double* qr
     if (jhi > qpos) jhi = qpos;
     if (jhi > L - 1) jhi = L - 1;
     if (jhi >= jlo) {
-      for (int d = 0; d < a->D; ++d)
+      for (int d = 0; d < a->D; ++d) {
         qrow[d] = elem(a->q, a->q_dtype, (t * a->Hq + h) * (int64_t)a->D + d);
+        if (a->q_dtype == ORC_MXFP4)             /* the group's shared scale */
+          qrow[d] *= orc_decode_e8m0(a->q_mx[(t * a->Hq + h) * (int64_t)(a->D / 32) + d / 32]);
+      }
       int64_t dst = d_stride(a);
       for (int64_t j = jlo; j <= jhi; ++j) {
         int64_t off, sidx;
         key_row(a, b, j, hk, &off, &sidx);
+        int64_t mxr = a->k_dtype == ORC_MXFP4 ? mx_key_row(a, b, j, hk) : 0;
         double dot = 0.0;                        /* DOT */
-        for (int d = 0; d < a->D; ++d) dot += qrow[d] * elem(a->k, a->k_dtype, off + d * dst);
+        for (int d = 0; d < a->D; ++d) {
+          double kv = elem(a->k, a->k_dtype, off + d * dst);
+          if (a->k_dtype == ORC_MXFP4) kv *= orc_decode_e8m0(a->k_mx[mxr + d / 32]);
+          dot += qrow[d] * kv;
+        }
         if (a->k_dtype == ORC_I8) dot *= (double)a->scale[sidx];   /* DEQUANT */
         if (dot > best) best = dot;              /* MAX over the visible j */
       }
@@ -311,7 +348,8 @@ int64_t orc_out_width(int64_t max_blocks) {
   a.Hkv = Hkv; a.P = P;                                                        \
   for (int i = 0; i < 4; ++i) a.ks[i] = k_strides[i];                          \
   a.start_loc = start_loc; a.block_table = block_table; a.MB = MB;             \
-  a.scale = scale; a.cu_q = cu_q; a.kv_len = kv_len; a.B = B;                  \
+  a.scale = scale; a.q_mx = q_mx; a.k_mx = k_mx;                              \
+  a.cu_q = cu_q; a.kv_len = kv_len; a.B = B;                                   \
   a.sparse_mode = sparse_mode; a.init_blocks = init_blocks;                    \
   a.local_blocks = local_blocks; a.local_mode = local_mode;                    \
   a.W = orc_out_width(MB);                                                     \
@@ -325,6 +363,7 @@ int orc_index_score(const void* q, int q_dtype, int64_t T, int Hq, int D,
                     const void* k, int k_dtype, int layout, int64_t k_dim0, int Hkv,
                     int P, const int64_t* k_strides, const int32_t* start_loc,
                     const int32_t* block_table, int64_t MB, const float* scale,
+                    const uint8_t* q_mx, const uint8_t* k_mx,
                     const int32_t* cu_q, const int32_t* kv_len, int B, int sparse_mode,
                     int init_blocks, int local_blocks, int local_mode, float* out,
                     int nthreads) {
@@ -339,6 +378,7 @@ int orc_index_score_points(const void* q, int q_dtype, int64_t T, int Hq, int D,
                            const void* k, int k_dtype, int layout, int64_t k_dim0, int Hkv,
                            int P, const int64_t* k_strides, const int32_t* start_loc,
                            const int32_t* block_table, int64_t MB, const float* scale,
+                           const uint8_t* q_mx, const uint8_t* k_mx,
                            const int32_t* cu_q, const int32_t* kv_len, int B,
                            int sparse_mode, int init_blocks, int local_blocks,
                            int local_mode, const int64_t* pts, int64_t n, float* vals,

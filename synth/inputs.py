@@ -16,6 +16,12 @@ Distributions (from the workload descriptions):
     the storage type; for fp8 e4m3 the float32 value is clamped to +-448 first.
   * int8 key: uniform integers in [-127, 127].
   * int8 scale: lognormal(mu=-6, sigma=0.5), float32.
+  * MXFP4 query/key: N(0, 1) in float32 encoded as OCP microscaling FP4 --
+    per group of 32 elements along D a shared E8M0 exponent
+    floor(log2(max|v|)) - 2 (E2M1's largest exponent) and the elements
+    divided by it and rounded to the nearest E2M1 value (ties to the even
+    code, saturating at 6); two elements per byte, the even one in the low
+    nibble.  This is the encoding of the inputs, not part of the operator.
 """
 from __future__ import annotations
 
@@ -31,6 +37,7 @@ DTYPES = {
     "i8": torch.int8,
     "f8e4m3": torch.float8_e4m3fn,
     "f8e5m2": torch.float8_e5m2,
+    "mxfp4": torch.uint8,               # packed E2M1 pairs, with E8M0 group scales
 }
 
 # The five workloads the operator is measured on, in order.
@@ -67,6 +74,8 @@ class MsaCase:
     gap: int = 0                        # unused pages between used ones (paged)
     poison: Optional[str] = None
     local_mode: int = 0                 # 0: window at start_loc; 1: at each token's block
+    q_mx_scale: Optional[torch.Tensor] = None   # MXFP4: uint8 E8M0 [T, Hq, D/32]
+    k_mx_scale: Optional[torch.Tensor] = None   # MXFP4: uint8 E8M0, key layout with D/32
 
     @property
     def batch(self) -> int:
@@ -88,7 +97,7 @@ class MsaCase:
 
     @property
     def D(self) -> int:
-        return int(self.query.shape[2])
+        return int(self.query.shape[2]) * (2 if self.query.dtype == torch.uint8 else 1)
 
     def key_dtype_name(self) -> str:
         return _dtype_name(self.key.dtype)
@@ -137,6 +146,42 @@ def _fill_values(out: torch.Tensor, rng: np.random.Generator):
         _fill_normal(out, rng, clamp=57344.0)
     else:
         _fill_normal(out, rng)
+
+
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
+
+
+def _encode_mxfp4(x: np.ndarray):
+    """float32 [n, D] -> (packed E2M1 uint8 [n, D/2], E8M0 uint8 [n, D/32])."""
+    n, D = x.shape
+    g = x.reshape(n, D // 32, 32)
+    amax = np.abs(g).max(axis=2)
+    _, ex = np.frexp(amax)                     # amax = m * 2^ex, m in [0.5, 1)
+    e = np.where(amax > 0, ex - 1, -127) - 2   # floor(log2 amax) - 2
+    code = np.clip(e + 127, 0, 254).astype(np.uint8)
+    v = g / np.exp2(code.astype(np.float32) - 127.0)[:, :, None]
+    a = np.minimum(np.abs(v), 6.0)
+    dist = np.abs(a[..., None] - _E2M1_MAG) + (np.arange(8) & 1) * 1e-6
+    idx = np.argmin(dist, axis=-1).astype(np.uint8)
+    nib = idx | (((v < 0) & (idx > 0)).astype(np.uint8) << 3)
+    nib = nib.reshape(n, D)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return packed, code
+
+
+def _fill_mxfp4(vals: torch.Tensor, scales: torch.Tensor, rng: np.random.Generator):
+    """vals uint8 [..., D/2], scales uint8 [..., D/32]: rows of N(0,1) encoded."""
+    half = vals.shape[-1]
+    fv = vals.reshape(-1, half)
+    fs = scales.reshape(-1, scales.shape[-1])
+    rows = fv.shape[0]
+    step = max(1, _CHUNK // (2 * half))
+    for i in range(0, rows, step):
+        m = min(step, rows - i)
+        x = rng.standard_normal(size=(m, 2 * half), dtype=np.float32)
+        pk, sc = _encode_mxfp4(x)
+        fv[i:i + m].copy_(torch.from_numpy(pk))
+        fs[i:i + m].copy_(torch.from_numpy(sc))
 
 
 def _fill_scale(out: torch.Tensor, rng: np.random.Generator):
@@ -210,20 +255,38 @@ def make_case(name: str, seed: int, *, q_lens: Sequence[int], kv_lens: Sequence[
         block_table = torch.from_numpy(bt.astype(np.int32)).contiguous()
 
     # 3. query
-    query = torch.empty((T, Hq, D), dtype=DTYPES[qdtype])
-    _fill_values(query, rng)
+    mx = qdtype == "mxfp4"
+    assert mx == (kdtype == "mxfp4"), "MXFP4 query and key go together"
+    Dq = D // 2 if mx else D                   # stored last axis (bytes for MXFP4)
+    query = torch.empty((T, Hq, Dq), dtype=DTYPES[qdtype])
+    q_mx = k_mx = None
+    if mx:
+        q_mx = torch.empty((T, Hq, D // 32), dtype=torch.uint8)
+        _fill_mxfp4(query, q_mx, rng)
+    else:
+        _fill_values(query, rng)
 
-    # 4. key
+    # 4. key (MXFP4: the scales are indexed by logical page, dim0 gaps or not)
     if layout == "TND":
         T2 = int(kv.sum())
-        key_storage = torch.empty((T2, Hkv, D), dtype=DTYPES[kdtype])
-        _fill_values(key_storage, rng)
+        key_storage = torch.empty((T2, Hkv, Dq), dtype=DTYPES[kdtype])
+        if mx:
+            k_mx = torch.empty((T2, Hkv, D // 32), dtype=torch.uint8)
+            _fill_mxfp4(key_storage, k_mx, rng)
+        else:
+            _fill_values(key_storage, rng)
         key = key_storage
     else:
         NPs = NP * (gap + 1)
-        shape = (NPs, P, Hkv, D) if layout == "BBND" else (NPs, Hkv, P, D)
+        shape = (NPs, P, Hkv, Dq) if layout == "BBND" else (NPs, Hkv, P, Dq)
         key_storage = torch.empty(shape, dtype=DTYPES[kdtype])
-        _fill_values(key_storage, rng)
+        if mx:
+            sshape = (NPs, P, Hkv, D // 32) if layout == "BBND" else (NPs, Hkv, P, D // 32)
+            full = torch.empty(sshape, dtype=torch.uint8)
+            _fill_mxfp4(key_storage, full, rng)
+            k_mx = (full[:: gap + 1] if gap else full).contiguous()
+        else:
+            _fill_values(key_storage, rng)
         key = key_storage[:: gap + 1] if gap else key_storage
 
     # 5. scale (int8 keys)
@@ -246,7 +309,8 @@ def make_case(name: str, seed: int, *, q_lens: Sequence[int], kv_lens: Sequence[
         kv_len=torch.from_numpy(kv.astype(np.int32)),
         start_loc=torch.from_numpy(sl.astype(np.int32)),
         max_blocks=int(MB), sparse_mode=sparse_mode, init_blocks=init_blocks,
-        local_blocks=local_blocks, block_size=P, gap=gap, local_mode=local_mode)
+        local_blocks=local_blocks, block_size=P, gap=gap, local_mode=local_mode,
+        q_mx_scale=q_mx, k_mx_scale=k_mx)
 
 
 def config_case(c: int) -> MsaCase:
@@ -284,11 +348,15 @@ def config_case(c: int) -> MsaCase:
 
 _POISON = {
     # pattern -> value per storage dtype
-    "zero": {"f16": 0.0, "bf16": 0.0, "f8e4m3": 0.0, "f8e5m2": 0.0, "i8": 0, "scale": 0.0},
+    # (MXFP4 values have no NaN: 0x77 is 6.0 twice, 0xFF is -6.0 twice; its
+    # E8M0 scales poison as 2^-127, 2^127 and the NaN code 255)
+    "zero": {"f16": 0.0, "bf16": 0.0, "f8e4m3": 0.0, "f8e5m2": 0.0, "i8": 0, "scale": 0.0,
+             "mxfp4": 0, "mx_scale": 0},
     "big": {"f16": 65504.0, "bf16": 3.0e38, "f8e4m3": 448.0, "f8e5m2": 57344.0, "i8": 127,
-            "scale": 3.0e38},
+            "scale": 3.0e38, "mxfp4": 0x77, "mx_scale": 254},
     "nan": {"f16": float("nan"), "bf16": float("nan"), "f8e4m3": float("nan"),
-            "f8e5m2": float("nan"), "i8": -128, "scale": float("nan")},
+            "f8e5m2": float("nan"), "i8": -128, "scale": float("nan"), "mxfp4": 0xFF,
+            "mx_scale": 255},
 }
 
 
@@ -310,6 +378,8 @@ def poison_case(case: MsaCase, pattern: str) -> MsaCase:
     key = ks[:: gap + 1] if gap else ks
     bt = case.block_table.clone()
     scale = case.scale.clone() if case.scale is not None else None
+    mxs = case.k_mx_scale.clone() if case.k_mx_scale is not None else None
+    mxv = _POISON[pattern]["mx_scale"]
     kname = case.key_dtype_name()
     kval = _POISON[pattern][kname]
     NP = int(key.shape[0])
@@ -328,6 +398,8 @@ def poison_case(case: MsaCase, pattern: str) -> MsaCase:
         ks[torch.from_numpy(unused)] = kval
     if scale is not None and unused.size:
         scale[torch.from_numpy(unused)] = _POISON[pattern]["scale"]
+    if mxs is not None and unused.size:
+        mxs[torch.from_numpy(unused)] = mxv
     k = 0
     for b in range(case.batch):
         L = int(kv[b])
@@ -341,11 +413,17 @@ def poison_case(case: MsaCase, pattern: str) -> MsaCase:
                 key[page, :, tail:] = kval
             if scale is not None:
                 scale[page, :, tail:] = _POISON[pattern]["scale"]
+            if mxs is not None:
+                if case.layout == "BBND":
+                    mxs[page, tail:] = mxv
+                else:
+                    mxs[page, :, tail:] = mxv
         if unused.size:
             for beta in range(nb, bt.shape[1]):
                 bt[b, beta] = int(unused[k % unused.size])
                 k += 1
     return dataclasses.replace(case, key=key, key_storage=ks, block_table=bt, scale=scale,
+                               k_mx_scale=mxs,
                                poison=pattern)
 
 
@@ -455,6 +533,19 @@ def edge_cases() -> List[MsaCase]:
         layout="BBND", extra_pages=6, init_blocks=1, local_blocks=2, local_mode=1)
     add("perq_prefill_bnbd_wide", q_lens=[260], kv_lens=[1000], Hq=8, Hkv=1, qdtype="bf16",
         layout="BNBD", MB=40, extra_pages=4, init_blocks=2, local_blocks=4, local_mode=1)
+    # MXFP4 query and key (E2M1 values, E8M0 scale per 32 elements)
+    add("mx_mix_bbnd", q_lens=[3, 1, 37], kv_lens=[300, 129, 600], Hq=8, Hkv=2,
+        qdtype="mxfp4", layout="BBND", extra_pages=4, init_blocks=1, local_blocks=2)
+    add("mx_mix_bnbd_gap", q_lens=[3, 1, 37], kv_lens=[300, 129, 600], Hq=8, Hkv=2,
+        qdtype="mxfp4", layout="BNBD", extra_pages=4, gap=1, init_blocks=1, local_blocks=2)
+    add("mx_prefill_tnd", q_lens=[300, 77], kv_lens=[556, 77], Hq=16, Hkv=2, qdtype="mxfp4",
+        layout="TND", init_blocks=1, local_blocks=2)
+    add("mx_q_longer_than_kv", q_lens=[10, 4], kv_lens=[6, 130], Hq=4, Hkv=1, qdtype="mxfp4",
+        layout="BBND", extra_pages=4, init_blocks=1, local_blocks=1)
+    add("mx_perq_prefill_bbnd", q_lens=[200], kv_lens=[450], Hq=16, Hkv=2, qdtype="mxfp4",
+        layout="BBND", extra_pages=6, init_blocks=1, local_blocks=2, local_mode=1)
+    add("mx_decode_g16", q_lens=[1] * 5, kv_lens=[1, 127, 128, 129, 700], Hq=16, Hkv=1,
+        qdtype="mxfp4", layout="BBND", extra_pages=3)
     return cs
 
 

@@ -16,18 +16,51 @@ def _round16(n):
     return (n + 15) // 16 * 16
 
 
+def _e2m1_as_e4m3fn(nib: torch.Tensor) -> torch.Tensor:
+    """float64 values of E2M1 codes through torch's e4m3fn decoder: an E2M1
+    code (sign s, exponent e, fraction f; bias 1) is the e4m3fn code (s,
+    e + 6, 4 f) (bias 7); its subnormal 0.5 (e = 0, f = 1) is e4m3fn (0, 6,
+    0) and its zero is zero."""
+    nib = nib.to(torch.int32)
+    s, e, f = (nib >> 3) & 1, (nib >> 1) & 3, nib & 1
+    code = torch.where(e > 0, (e + 6) << 3 | (f << 2), torch.where(f > 0, 6 << 3, 0))
+    code = code | (s << 7)
+    return code.to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def decode_mxfp4(vals: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """Packed E2M1 [..., D/2] (even element in the low nibble) with E8M0
+    group scales [..., D/32] -> float64 [..., D]; scales via torch's e8m0."""
+    lo, hi = vals & 15, vals >> 4
+    nib = torch.stack([lo, hi], dim=-1).reshape(*vals.shape[:-1], vals.shape[-1] * 2)
+    x = _e2m1_as_e4m3fn(nib)
+    sc = scales.view(torch.float8_e8m0fnu).to(torch.float64)
+    return x * sc.repeat_interleave(32, dim=-1)
+
+
+def _query(case, t0, t1):
+    if case.query.dtype == torch.uint8:
+        return decode_mxfp4(case.query[t0:t1], case.q_mx_scale[t0:t1])
+    return case.query[t0:t1].to(torch.float64)
+
+
 def request_keys(case, b):
     """Dequantised keys k~ of request b as float64 [L, Hkv, D]."""
     P = case.block_size
     L = int(case.kv_len[b])
     nb = -(-L // P)
+    mx = case.key.dtype == torch.uint8
     if case.layout == "TND":
         off = int(case.kv_len[:b].sum())
-        k = case.key[off:off + L].to(torch.float64)
+        k = (decode_mxfp4(case.key[off:off + L], case.k_mx_scale[off:off + L]) if mx
+             else case.key[off:off + L].to(torch.float64))
         s = case.scale[off:off + L].to(torch.float64) if case.scale is not None else None
     else:
         pages = case.block_table[b, :nb].long()
-        kp = case.key[pages].to(torch.float64)              # [nb, P, Hkv, D] or [nb, Hkv, P, D]
+        if mx:
+            kp = decode_mxfp4(case.key[pages], case.k_mx_scale[pages])
+        else:
+            kp = case.key[pages].to(torch.float64)          # [nb, P, Hkv, D] or [nb, Hkv, P, D]
         if case.layout == "BNBD":
             kp = kp.permute(0, 2, 1, 3)
         k = kp.reshape(nb * P, kp.shape[2], kp.shape[3])[:L]
@@ -52,7 +85,7 @@ def brute_force(case) -> torch.Tensor:
         if Lq == 0 or L == 0:
             continue
         nb = -(-L // P)
-        q = case.query[t0:t1].to(torch.float64)              # [Lq, Hq, D]
+        q = _query(case, t0, t1)                              # [Lq, Hq, D]
         k = request_keys(case, b)                             # [L, Hkv, D]
         kh = k.repeat_interleave(g, dim=1)                    # [L, Hq, D]
         s = torch.matmul(q.permute(1, 0, 2), kh.permute(1, 2, 0))   # [Hq, Lq, L]

@@ -46,13 +46,23 @@ MUTANTS = {
                                   "int64_t pos = (a->sparse_mode == 3) ? L - Lq + i : L - 1;"),
     "per_query_negative_to_block0": ("s = pos >= 0 ? pos / a->P : -1;",
                                      "s = pos >= 0 ? pos / a->P : 0;"),
+    # MXFP4
+    "mx_nibble_order": ("[i >> 1] >> (4 * (i & 1))) & 15);", "[i >> 1] >> (4 * (~i & 1))) & 15);"),
+    "mx_e2m1_subnormal": ("double v = e == 0 ? 0.5 * f :", "double v = e == 0 ? 1.0 * f :"),
+    "mx_e8m0_bias": ("ldexp(1.0, (int)e - 127); }", "ldexp(1.0, (int)e - 128); }"),
+    "mx_query_group": ("(int64_t)(a->D / 32) + d / 32]);", "(int64_t)(a->D / 32) + d / 64]);"),
+    "mx_key_scale_bbnd_axes": ("return ((page * a->P + jj) * a->Hkv + hk) * groups;",
+                               "return ((page * a->Hkv + hk) * a->P + jj) * groups;"),
+    "mx_key_scale_dropped": ("if (a->k_dtype == ORC_MXFP4) kv *= orc_decode_e8m0(a->k_mx[mxr + d / 32]);",
+                             ""),
 }
 
 CASE_NAMES = ["tiny_bbnd_f16", "mix_bbnd_bf16", "mix_bnbd_bf16", "mix_tnd_bf16",
               "mix_bbnd_i8", "mix_bnbd_i8", "mix_tnd_i8", "mix_bbnd_f8e4m3",
               "pad_tnd_kvlen0", "q_longer_than_kv", "init_local_overlap", "mode0_tnd",
               "gqa_g3_bbnd", "gqa_g40_bbnd", "dim0_gap2_bnbd_i8",
-              "perq_prefill_tnd", "perq_mode0_bbnd", "perq_q_longer_than_kv"]
+              "perq_prefill_tnd", "perq_mode0_bbnd", "perq_q_longer_than_kv",
+              "mx_mix_bbnd", "mx_mix_bnbd_gap", "mx_prefill_tnd"]
 
 
 @pytest.fixture(scope="module")
@@ -84,6 +94,13 @@ def _agrees(lib, cases) -> bool:
         if not np.array_equal(np.isnan(w), np.isnan(g)) or not np.array_equal(
                 w[~np.isnan(w)], g[~np.isnan(g)]):
             return False
+    # MXFP4 packing (a reading: the even element in the low nibble).  A swap
+    # applied to query and key alike leaves every score unchanged, so the
+    # order is pinned on the element decoder: byte 0x21 holds E2M1 codes 1
+    # (0.5) then 2 (1.0).
+    g = oracle.decode(torch.tensor([0x21, 0xF0], dtype=torch.uint8), lib=lib)
+    if list(g[:4]) != [0.5, 1.0, 0.0, -6.0]:
+        return False
     return True
 
 

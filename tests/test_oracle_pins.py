@@ -360,3 +360,29 @@ def test_contract_violation_raises():
     bad = dataclasses.replace(c, kv_len=torch.tensor([1000], dtype=torch.int32))
     with pytest.raises(ValueError):
         oracle.index_score_case(bad)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 element and scale decoders
+# ---------------------------------------------------------------------------
+
+def test_e2m1_decoder_matches_the_e4m3fn_route():
+    # An E2M1 code (bias 1) is the e4m3fn code with exponent + 6 and the
+    # fraction bit moved up (tests/brute.py), which torch decodes.
+    from brute import _e2m1_as_e4m3fn
+    lib = oracle.load()
+    codes = torch.arange(16, dtype=torch.uint8)
+    want = _e2m1_as_e4m3fn(codes).tolist()
+    got = [lib.orc_decode_e2m1(int(c)) for c in codes]
+    assert got == want
+    # the format's shape: largest 6, smallest positive 0.5, symmetric
+    assert max(got) == 6.0 and min(x for x in got if x > 0) == 0.5
+    assert [abs(x) for x in got[8:]] == got[:8] and all(x <= 0 for x in got[8:])
+
+
+def test_e8m0_decoder_matches_torch():
+    lib = oracle.load()
+    codes = torch.arange(256, dtype=torch.uint8)
+    want = codes.view(torch.float8_e8m0fnu).to(torch.float64).tolist()
+    got = [lib.orc_decode_e8m0(int(c)) for c in codes]
+    assert all((g == w) or (g != g and w != w) for g, w in zip(got, want))
