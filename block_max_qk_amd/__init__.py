@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     msa_block_topk,
     msa_index_score,
     msa_index_score_kernel_family,
+    msa_index_score_mxfp4,
     msa_index_score_out_width,
     msa_status_str,
 )

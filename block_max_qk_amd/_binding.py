@@ -24,13 +24,14 @@ DTYPE_CODE = {
     torch.int8: 2,
     torch.float8_e4m3fn: 3,
     torch.float8_e5m2: 4,
+    torch.uint8: 5,          # MXFP4: E2M1 pairs, with E8M0 group scales alongside
 }
 LAYOUT_CODE = {"TND": 0, "BBND": 1, "BNBD": 2}
 STATUS_NAMES = ["MSA_OK", "MSA_ERR_NULL", "MSA_ERR_LAYOUT", "MSA_ERR_DTYPE", "MSA_ERR_SHAPE",
                 "MSA_ERR_STRIDE", "MSA_ERR_SCALE", "MSA_ERR_ATTR", "MSA_ERR_HIP"]
 EXPORTED = ("msa_index_score", "msa_index_score_family", "msa_index_score_ex",
-            "msa_index_score_out_width", "msa_status_str", "msa_index_score_kernel_family",
-            "msa_block_topk")
+            "msa_index_score_mxfp4", "msa_index_score_out_width", "msa_status_str",
+            "msa_index_score_kernel_family", "msa_block_topk")
 LOCAL_MODE_CODE = {"request": 0, "query": 1}
 
 
@@ -76,6 +77,11 @@ def load_library(path: Optional[str] = None):
         lib.msa_index_score_ex.argtypes = (args[:13] + [ctypes.c_int32] + args[13:] +
                                            [ctypes.c_int32])
         lib.msa_index_score_ex.restype = ctypes.c_int
+        lib.msa_index_score_mxfp4.argtypes = [
+            ctypes.POINTER(MsaTensor), ptr, ctypes.POINTER(MsaTensor), ptr, ptr, ptr,
+            ctypes.c_int64, ptr, ptr, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ptr, ctypes.c_int64, ptr]
+        lib.msa_index_score_mxfp4.restype = ctypes.c_int
         lib.msa_index_score_out_width.argtypes = [ctypes.c_int64]
         lib.msa_index_score_out_width.restype = ctypes.c_int64
         lib.msa_status_str.argtypes = [ctypes.c_int32]
@@ -167,6 +173,50 @@ def msa_index_score(query: torch.Tensor, key: torch.Tensor, start_loc: torch.Ten
         st = lib.msa_index_score(*args)
     else:
         st = lib.msa_index_score_family(*args, int(family))
+    if st != 0:
+        cls = MsaLayoutError if st == 2 else MsaError
+        raise cls(st, msa_status_str(st))
+    return out
+
+
+def msa_index_score_mxfp4(query: torch.Tensor, query_scale: torch.Tensor, key: torch.Tensor,
+                          key_scale: torch.Tensor, start_loc: Optional[torch.Tensor],
+                          block_table: Optional[torch.Tensor], cu_seqlens_q: torch.Tensor,
+                          kv_len: torch.Tensor, layout, sparse_mode: int, init_blocks: int,
+                          local_blocks: int, out: torch.Tensor, max_blocks: int, stream=None,
+                          local_mode=0) -> torch.Tensor:
+    """The MXFP4 entry: ``query`` [T, Hq, 64] and ``key`` (layout-shaped, last
+    axis 64) uint8 hold E2M1 pairs; ``query_scale`` [T, Hq, 4] and
+    ``key_scale`` (the key's layout with a last axis of 4) uint8 hold E8M0."""
+    lib = load_library()
+    dev = out.device
+    for name, t in (("query", query), ("query_scale", query_scale), ("key", key),
+                    ("key_scale", key_scale), ("start_loc", start_loc),
+                    ("cu_seqlens_q", cu_seqlens_q), ("kv_len", kv_len),
+                    ("block_table", block_table)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, out on {dev}")
+    for name, t in (("query", query), ("key", key), ("query_scale", query_scale),
+                    ("key_scale", key_scale)):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be uint8 (MXFP4 values / E8M0 scales)")
+    for name, t in (("query_scale", query_scale), ("key_scale", key_scale)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.dim() != 3:
+        raise ValueError("out must be a contiguous float32 [Hq, T, W] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    lm = LOCAL_MODE_CODE.get(local_mode, -1) if isinstance(local_mode, str) else int(local_mode)
+    qd, kd = describe(query), describe(key)
+    st = lib.msa_index_score_mxfp4(
+        ctypes.byref(qd), _ptr(query_scale), ctypes.byref(kd), _ptr(key_scale),
+        _ptr(start_loc), _ptr(block_table), int(max_blocks), _ptr(cu_seqlens_q),
+        _ptr(kv_len), int(kv_len.numel()), _layout_code(layout), int(sparse_mode),
+        int(init_blocks), int(local_blocks), lm, _ptr(out), int(out.shape[2]),
+        ctypes.c_void_p(stream))
     if st != 0:
         cls = MsaLayoutError if st == 2 else MsaError
         raise cls(st, msa_status_str(st))

@@ -18,7 +18,7 @@ constexpr int kP = 128;   // tokens per logical block
 constexpr int kD = 128;   // index head dimension
 
 // Element kinds of the key (the query kind follows from it).
-enum KeyKind : int { KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4 };
+enum KeyKind : int { KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4, KMXFP4 = 5 };
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -44,6 +44,13 @@ struct Params {
   int64_t s_page_stride;       // scale elements between pages (paged)
   int32_t s_row_stride;        // scale elements between tokens
   int32_t s_head_stride;       // scale elements between KV heads
+  // MXFP4: E8M0 scales, one byte per 32 elements, a token row's D/32 bytes
+  // contiguous; query [T, Hq, D/32]; key strides in bytes (page by logical
+  // page index)
+  const uint8_t* q_mx;
+  const uint8_t* k_mx;
+  int64_t mx_page_stride;
+  int32_t mx_row_stride, mx_head_stride;
   int64_t T;
   int32_t B, Hq, Hkv, g;
   int32_t MB, W;
@@ -318,12 +325,24 @@ __device__ __forceinline__ f32x16 mfma32x32x64_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fmt, fmt, 0, 0, 0, 0);
 }
 
+// MXFP4 (E2M1) operands with per-lane E8M0 scales (byte 0 of sa / sb):
+// lane l covers row l % 32 and the 32 elements 32 (l / 32) + [0, 32) of the
+// 64-deep k step, 16 bytes, two elements per byte (the even one in the low
+// nibble); the scale is that group's.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp4(i32x4 a, i32x4 b, f32x16 c, int sa, int sb) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+
 template <int KK>
 struct Kind {
   static constexpr bool is_f8 = (KK == KF8E4M3 || KK == KF8E5M2);
   static constexpr bool is_i8 = (KK == KI8);
-  static constexpr int q_bytes = is_f8 ? 1 : 2;   // query element size
+  static constexpr bool is_fp4 = (KK == KMXFP4);
+  static constexpr int q_bytes = is_f8 ? 1 : 2;   // query element size (not MXFP4)
   static constexpr int k_bytes = (is_f8 || is_i8) ? 1 : 2;
+  static constexpr int q_row = is_fp4 ? kD / 2 : kD * q_bytes;   // bytes per query row
   static constexpr int mfma_kind = is_i8 ? KF16 : KK;  // operand type fed to MFMA
 };
 

@@ -27,7 +27,8 @@ int elem_bytes(int32_t dt) {
     case MSA_DTYPE_BF16: return 2;
     case MSA_DTYPE_I8:
     case MSA_DTYPE_F8E4M3:
-    case MSA_DTYPE_F8E5M2: return 1;
+    case MSA_DTYPE_F8E5M2:
+    case MSA_DTYPE_MXFP4: return 1;   // MXFP4: a byte holds two elements
     default: return 0;
   }
 }
@@ -40,6 +41,7 @@ bool pair_ok(int32_t qd, int32_t kd) {
   if (qd == MSA_DTYPE_BF16 && kd == MSA_DTYPE_BF16) return true;
   if (qd == MSA_DTYPE_F8E4M3 && kd == MSA_DTYPE_F8E4M3) return true;
   if (qd == MSA_DTYPE_F8E5M2 && kd == MSA_DTYPE_F8E5M2) return true;
+  if (qd == MSA_DTYPE_MXFP4 && kd == MSA_DTYPE_MXFP4) return true;
   return false;
 }
 
@@ -79,6 +81,7 @@ hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
 
 msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32_t* start_loc,
                  const int32_t* block_table, int64_t max_blocks, const float* scale,
+                 const uint8_t* q_mx, const uint8_t* k_mx,
                  const int32_t* cu_seqlens_q, const int32_t* kv_len, int32_t batch,
                  int32_t layout, int32_t sparse_mode, int32_t init_blocks,
                  int32_t local_blocks, int32_t local_mode, float* out, int64_t out_width,
@@ -99,11 +102,16 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (!pair_ok(query->dtype, key->dtype)) return MSA_ERR_DTYPE;
   const bool is_i8 = key->dtype == MSA_DTYPE_I8;
   if (is_i8 != (scale != nullptr)) return MSA_ERR_SCALE;
+  // MXFP4 takes its E8M0 group scales (and nothing else does); its last axis
+  // holds D/2 bytes
+  const bool is_mx = key->dtype == MSA_DTYPE_MXFP4;
+  if (is_mx != (q_mx != nullptr) || is_mx != (k_mx != nullptr)) return MSA_ERR_SCALE;
+  const int64_t DB = is_mx ? msa::kD / 2 : msa::kD;     // stored last-axis extent
 
   // query [T, Hq, D], compact
   if (query->ndim != 3) return MSA_ERR_SHAPE;
   const int64_t T = query->shape[0], Hq = query->shape[1], D = query->shape[2];
-  if (T < 0 || Hq < 1 || D != msa::kD) return MSA_ERR_SHAPE;
+  if (T < 0 || Hq < 1 || D != DB) return MSA_ERR_SHAPE;
   if (!compact_axis(D, query->stride[2], 1) || !compact_axis(Hq, query->stride[1], D) ||
       !compact_axis(T, query->stride[0], Hq * D))
     return MSA_ERR_STRIDE;
@@ -117,7 +125,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
     NP = key->shape[0];
     Hkv = key->shape[1];
     KD = key->shape[2];
-    if (Hkv < 1 || KD != msa::kD || NP < 0) return MSA_ERR_SHAPE;
+    if (Hkv < 1 || KD != DB || NP < 0) return MSA_ERR_SHAPE;
     if (!compact_axis(KD, ks[2], 1) || !compact_axis(Hkv, ks[1], KD) ||
         !compact_axis(NP, ks[0], Hkv * KD))
       return MSA_ERR_STRIDE;
@@ -129,7 +137,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
     P = key->shape[1];
     Hkv = 1;
     KD = key->shape[2];
-    if (P != msa::kP || KD != msa::kD || NP < 1) return MSA_ERR_SHAPE;
+    if (P != msa::kP || KD != DB || NP < 1) return MSA_ERR_SHAPE;
     if (!compact_axis(KD, ks[2], 1) || !compact_axis(P, ks[1], KD)) return MSA_ERR_STRIDE;
     s_page = ks[0];
     s_row = KD;
@@ -145,7 +153,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
       Hkv = key->shape[1];
       P = key->shape[2];
     }
-    if (P != msa::kP || KD != msa::kD || Hkv < 1 || NP < 1) return MSA_ERR_SHAPE;
+    if (P != msa::kP || KD != DB || Hkv < 1 || NP < 1) return MSA_ERR_SHAPE;
     if (!compact_axis(KD, ks[3], 1)) return MSA_ERR_STRIDE;
     if (layout == MSA_LAYOUT_BBND) {
       if (!compact_axis(Hkv, ks[2], KD) || !compact_axis(P, ks[1], Hkv * KD))
@@ -181,27 +189,42 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (init_blocks < 0 || local_blocks < 0 || init_blocks > limit || local_blocks > limit)
     return MSA_ERR_ATTR;
   if (family < -1 || family > 1) return MSA_ERR_ATTR;
+  if (is_mx && family == 0) return MSA_ERR_ATTR;   // MXFP4 runs on the prefill tiles only
   if (local_mode != MSA_LOCAL_PER_REQUEST && local_mode != MSA_LOCAL_PER_QUERY)
     return MSA_ERR_ATTR;
 
   // sizes the kernels index with 32-bit integers
   if (W > (1 << 24) || Hq > (1 << 16) || batch > (1 << 30) || T > (int64_t(1) << 31) - 1 ||
-      (msa::kP - 1) * s_row * kb + msa::kD * kb > INT32_MAX || s_head * kb > INT32_MAX)
+      (msa::kP - 1) * s_row * kb + DB * kb > INT32_MAX || s_head * kb > INT32_MAX)
     return MSA_ERR_SHAPE;
 
   if (!aligned16(query->data) || !aligned16(key->data) || !aligned16(out))
+    return MSA_ERR_STRIDE;
+  if ((reinterpret_cast<uintptr_t>(q_mx) & 3u) || (reinterpret_cast<uintptr_t>(k_mx) & 3u))
     return MSA_ERR_STRIDE;
 
   if (T == 0) return MSA_OK;
 
   // plan
   const int32_t g = (int32_t)(Hq / Hkv);
-  const int fam = family >= 0 ? family : choose_family(T, batch, g);
-  const int rows = fam == 1 ? msa::prefill_rows(key->dtype) : msa::kDecodeRows;
+  const int fam = is_mx ? 1 : family >= 0 ? family : choose_family(T, batch, g);
+  const int rows = fam == 1 ? msa::prefill_rows(is_mx ? msa::KMXFP4 : key->dtype)
+                            : msa::kDecodeRows;
   Params p{};
   p.q = static_cast<const uint8_t*>(query->data);
   p.k = static_cast<const uint8_t*>(key->data);
   p.scale = scale;
+  p.q_mx = q_mx;
+  p.k_mx = k_mx;
+  if (layout == MSA_LAYOUT_BNBD) {   // key scales [NP, Hkv, P, D/32]
+    p.mx_row_stride = msa::kD / 32;
+    p.mx_head_stride = msa::kP * (msa::kD / 32);
+    p.mx_page_stride = Hkv * msa::kP * (msa::kD / 32);
+  } else {                           // [NP, P, Hkv, D/32] or [T2, Hkv, D/32]
+    p.mx_row_stride = (int32_t)(Hkv * (msa::kD / 32));
+    p.mx_head_stride = msa::kD / 32;
+    p.mx_page_stride = paged ? msa::kP * Hkv * (msa::kD / 32) : 0;
+  }
   p.block_table = paged ? block_table : nullptr;
   p.cu_q = cu_seqlens_q;
   p.kv_len = kv_len;
@@ -238,7 +261,8 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   // head, head chunk), each walking its own copy of the batch's work list
   // fp8 prefill amortises each work item's query tile and set-up over more
   // blocks (measured faster); 16-bit keys balance better with 16
-  p.chunk = (fam == 1 && (key->dtype == MSA_DTYPE_F8E4M3 || key->dtype == MSA_DTYPE_F8E5M2))
+  p.chunk = (fam == 1 && (key->dtype == MSA_DTYPE_F8E4M3 || key->dtype == MSA_DTYPE_F8E5M2 ||
+                          is_mx))
                 ? 2 * msa::kPrefillChunk
                 : msa::kPrefillChunk;
   p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
@@ -256,6 +280,11 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
     case MSA_DTYPE_BF16: e = launch<msa::KBF16>(fam, p, grid, s); break;
     case MSA_DTYPE_I8: e = launch<msa::KI8>(fam, p, grid, s); break;
     case MSA_DTYPE_F8E4M3: e = launch<msa::KF8E4M3>(fam, p, grid, s); break;
+    case MSA_DTYPE_MXFP4:
+      hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4>, dim3((unsigned)grid), dim3(256), 0, s,
+                         p);
+      e = hipGetLastError();
+      break;
     default: e = launch<msa::KF8E5M2>(fam, p, grid, s); break;
   }
   return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
@@ -272,9 +301,9 @@ msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
                              int32_t batch, int32_t layout, int32_t sparse_mode,
                              int32_t init_blocks, int32_t local_blocks, float* out,
                              int64_t out_width, void* stream) {
-  return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
-             layout, sparse_mode, init_blocks, local_blocks, MSA_LOCAL_PER_REQUEST, out,
-             out_width, stream, -1);
+  return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
+             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
+             MSA_LOCAL_PER_REQUEST, out, out_width, stream, -1);
 }
 
 msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_t* key,
@@ -284,9 +313,9 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int32_t batch, int32_t layout, int32_t sparse_mode,
                                     int32_t init_blocks, int32_t local_blocks, float* out,
                                     int64_t out_width, void* stream, int32_t family) {
-  return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
-             layout, sparse_mode, init_blocks, local_blocks, MSA_LOCAL_PER_REQUEST, out,
-             out_width, stream, family);
+  return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
+             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
+             MSA_LOCAL_PER_REQUEST, out, out_width, stream, family);
 }
 
 msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* key,
@@ -296,9 +325,9 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
                                 int32_t batch, int32_t layout, int32_t sparse_mode,
                                 int32_t init_blocks, int32_t local_blocks, int32_t local_mode,
                                 float* out, int64_t out_width, void* stream, int32_t family) {
-  return run(query, key, start_loc, block_table, max_blocks, scale, cu_seqlens_q, kv_len, batch,
-             layout, sparse_mode, init_blocks, local_blocks, local_mode, out, out_width, stream,
-             family);
+  return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
+             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
+             local_mode, out, out_width, stream, family);
 }
 
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
@@ -346,6 +375,22 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
     hipLaunchKernelGGL((msa::topk_kernel<0, 1>), grid, block, 0, s, scores, T, Hq, width, nv, k, out);
 #undef MSA_TOPK_LAUNCH
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+}
+
+msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* query_scale,
+                                   const msa_tensor_t* key, const uint8_t* key_scale,
+                                   const int32_t* start_loc, const int32_t* block_table,
+                                   int64_t max_blocks, const int32_t* cu_seqlens_q,
+                                   const int32_t* kv_len, int32_t batch, int32_t layout,
+                                   int32_t sparse_mode, int32_t init_blocks,
+                                   int32_t local_blocks, int32_t local_mode, float* out,
+                                   int64_t out_width, void* stream) {
+  if (!query || !key) return MSA_ERR_NULL;
+  if (query->dtype != MSA_DTYPE_MXFP4 || key->dtype != MSA_DTYPE_MXFP4) return MSA_ERR_DTYPE;
+  if (!query_scale || !key_scale) return MSA_ERR_NULL;
+  return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
+             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
+             local_mode, out, out_width, stream, -1);
 }
 
 int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }

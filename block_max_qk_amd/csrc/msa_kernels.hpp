@@ -490,17 +490,19 @@ void prefill_kernel(Params p) {
   constexpr int NTW = prefill_ntw(KK);
   // Key blocks pass through an LDS ring of stages.  16-bit keys: stages of 64
   // tokens (16 KB), three deep, so a stage's copy has two compute periods to
-  // land; fp8: whole 128-token blocks (16 KB), two deep; int8 (widened to
-  // fp16 through registers): whole blocks (32 KB), two deep.  All of it fits
-  // three workgroups per CU (two for int8).
-  constexpr int RB = Kd::is_f8 ? 128 : 256;    // LDS bytes per key token
+  // land; fp8: whole 128-token blocks (16 KB), two deep; MXFP4: whole blocks
+  // (8 KB of values plus 512 B of scales), two deep; int8 (widened to fp16
+  // through registers): whole blocks (32 KB), two deep.  All of it fits three
+  // workgroups per CU (two for int8).
+  constexpr int RB = Kd::is_fp4 ? 64 : (Kd::is_f8 ? 128 : 256);   // LDS bytes per key token
   constexpr bool ASYNC = !Kd::is_i8;           // copy HBM/L2 -> LDS directly
   constexpr int ST = (ASYNC && RB == 256) ? 64 : kP;   // tokens per stage
   constexpr int SPB = kP / ST;                 // stages per block
   constexpr int RING = SPB == 2 ? 3 : 2;
   constexpr int SBYTES = ST * RB;
   constexpr int NI = SBYTES / 1024 / 4;        // copy instructions per wave per stage
-  static_assert(!ASYNC || NI == 4, "the ring's wait counts assume four copies per wave per stage");
+  static_assert(!ASYNC || RING == 2 || NI == 4,
+                "the three-deep ring's wait counts assume four copies per wave per stage");
   __shared__ __attribute__((aligned(16))) uint8_t kl[RING * SBYTES];
   __shared__ float scl[2][kP];
 
@@ -522,6 +524,7 @@ void prefill_kernel(Params p) {
 
   int lim[NTW];
   i32x4 qv[NTW][8];
+  int qsc[NTW][2];               // MXFP4: the query scale of each k step
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const int r = wave * 32 * NTW + nt * 32 + n;
@@ -531,10 +534,19 @@ void prefill_kernel(Params p) {
     lim[nt] = ok ? last_visible(p, w, i0 + ti) : -1;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qv[nt][s] = i32x4{0, 0, 0, 0};
+    qsc[nt][0] = qsc[nt][1] = 127;
     if (ok && busy) {
-      const uint8_t* qr =
-          p.q + ((int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg)) * kD * Kd::q_bytes;
-      if constexpr (Kd::is_f8) {
+      const int64_t qrow = (int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg);
+      const uint8_t* qr = p.q + qrow * Kd::q_row;
+      if constexpr (Kd::is_fp4) {
+        // k step s (64 deep) of group G: bytes [32s + 16G, +16), scale 2s + G
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(p.q_mx + qrow * (kD / 32));
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          qv[nt][s] = ld16(qr + 32 * s + 16 * G);
+          qsc[nt][s] = (sw >> (8 * (2 * s + G))) & 255;
+        }
+      } else if constexpr (Kd::is_f8) {
         // k step s (64 deep) of group G: bytes [64s + 32G, +32)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -589,16 +601,38 @@ void prefill_kernel(Params p) {
     const int X = wave * NI + q;
     const int jl = X * RPI + l / (RB / 16);         // token within the stage
     const int pos = l % (RB / 16);
-    const int c = pos ^ (RB == 256 ? (jl & 15) : ((jl >> 1) & 7));
+    const int c = pos ^ (RB == 256 ? (jl & 15) : RB == 128 ? ((jl >> 1) & 7) : ((jl >> 2) & 3));
     const int jj = off + jl;
     const int src = jj < nvalid ? jj : 0;
     __builtin_amdgcn_global_load_lds(
         reinterpret_cast<const void*>(kb + (uint32_t)(src * p.k_row_stride + 16 * c)),
         (__attribute__((address_space(3))) void*)(kl + slot * SBYTES + X * 1024), 16, 0, 0);
   };
+  // MXFP4: the scale words of this lane's key token in each of the block's
+  // four M tiles (token 32 mt + n), loaded into registers one stage ahead,
+  // with that stage's copies (rows past kv_len read row 0).  (Staged in LDS
+  // instead, the copies made every later LDS read of the stage wait for
+  // them.)
+  uint32_t ksw_next[Kd::is_fp4 ? 4 : 1];
+  auto load_scales = [&](int sg) {
+    const int beta = w.c0 + sg / SPB;
+    const int64_t base =
+        (p.paged ? (int64_t)__builtin_amdgcn_readlane(pidx, beta - w.c0) * p.mx_page_stride
+                 : (w.koff + (int64_t)beta * kP) * p.mx_row_stride) +
+        (int64_t)w.hk * p.mx_head_stride;
+    const uint8_t* sb = p.k_mx + uniform64(base);
+    const int nvalid = min(kP, w.L - beta * kP);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int jj = mt * 32 + n;
+      const int src = jj < nvalid ? jj : 0;
+      ksw_next[mt] = *reinterpret_cast<const uint32_t*>(sb + (uint32_t)(src * p.mx_row_stride));
+    }
+  };
   auto stage_async = [&](int sg, int slot, int64_t kbytes) {
 #pragma unroll
     for (int q = 0; q < NI; ++q) stage_copy(q, sg, slot, kbytes);
+    if constexpr (Kd::is_fp4) load_scales(sg);
   };
   auto gload_i8 = [&](int beta) {
     const uint8_t* kb = p.k + block_bytes(beta) + (int64_t)w.hk * p.k_head_stride;
@@ -734,13 +768,17 @@ void prefill_kernel(Params p) {
       // of a 32-byte operand.  Fragment i + LEAD is read from LDS while
       // fragment i feeds the MFMAs, which hides the LDS latency with only
       // LEAD + 1 fragments live.
-      constexpr int PER_MT = Kd::is_f8 ? 4 : 8; // fragments per M tile
+      constexpr int PER_MT = Kd::is_fp4 ? 2 : Kd::is_f8 ? 4 : 8;   // fragments per M tile
       constexpr int NFR = (ST / 32) * PER_MT;
-      constexpr int LEAD = Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
+      constexpr int LEAD = Kd::is_fp4 ? 2 : Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
       auto frag = [&](int i) -> i32x4 {
         const int mt = i / PER_MT, q = i % PER_MT;
         const int jj = mt * 32 + n;
-        if constexpr (Kd::is_f8) {
+        if constexpr (Kd::is_fp4) {
+          // q = k step s: bytes [32s + 16G, +16) of the token, chunk 2s + G
+          const int c = 2 * q + G;
+          return *reinterpret_cast<const i32x4*>(kc + jj * 64 + ((c ^ ((jj >> 2) & 3)) << 4));
+        } else if constexpr (Kd::is_f8) {
           // q = 2*s + half: bytes [64s + 32G + 16*half, +16) of the token
           const int c = 4 * (q >> 1) + 2 * G + (q & 1);
           return *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ ((jj >> 1) & 7)) << 4));
@@ -753,6 +791,12 @@ void prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
       f32x16 acc[NTW];
+      // MXFP4: this block's scale words (loaded during the previous stage)
+      uint32_t ksw[Kd::is_fp4 ? 4 : 1];
+      if constexpr (Kd::is_fp4) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ksw[mt] = ksw_next[mt];
+      }
 #pragma unroll
       for (int i = 0; i < NFR; ++i) {
         if constexpr (ASYNC) {
@@ -764,6 +808,9 @@ void prefill_kernel(Params p) {
 #pragma unroll
             for (int q = 0; q < NI / CPTS; ++q)
               stage_copy((i / (NFR / CPTS)) * (NI / CPTS) + q, csg, csg % RING, ckb);
+            if constexpr (Kd::is_fp4) {
+              if (i == 0) load_scales(csg);
+            }
           }
         }
         if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
@@ -772,7 +819,13 @@ void prefill_kernel(Params p) {
 #pragma unroll
           for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x16{};
         }
-        if constexpr (Kd::is_f8) {
+        if constexpr (Kd::is_fp4) {
+          // byte 2q + G of the token's scale word is this lane's group
+          const int sa = (ksw[mt] >> (8 * (2 * q + G))) & 255;
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            acc[nt] = mfma32x32x64_fp4(f[i], qv[nt][q], acc[nt], sa, qsc[nt][q]);
+        } else if constexpr (Kd::is_f8) {
           if (q & 1) {
             const int s = q >> 1;
             const i32x8 a = cat(f[i - 1], f[i]);

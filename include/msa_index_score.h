@@ -73,7 +73,8 @@ typedef enum {
   MSA_DTYPE_BF16 = 1,
   MSA_DTYPE_I8 = 2,
   MSA_DTYPE_F8E4M3 = 3,
-  MSA_DTYPE_F8E5M2 = 4
+  MSA_DTYPE_F8E5M2 = 4,
+  MSA_DTYPE_MXFP4 = 5  /* E2M1 pairs, one byte each; see msa_index_score_mxfp4 */
 } msa_dtype_t;
 
 /* A strided view of device memory.  `data` points at element [0, 0, ...];
@@ -169,6 +170,44 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
                                 int32_t batch, int32_t layout, int32_t sparse_mode,
                                 int32_t init_blocks, int32_t local_blocks, int32_t local_mode,
                                 float* out, int64_t out_width, void* stream, int32_t family);
+
+/* The block score on MXFP4 index vectors: the FP4 indexer variant of the
+ * notes "MiniMax Sparse Attention: paper algorithm and code" (section 4.6,
+ * path B, and section 8.2: MXFP4 is E2M1 values with an E8M0 scale per group
+ * of elements, the block scores stay float32).  Same definition as
+ * msa_index_score, with q and k~ the decoded MXFP4 vectors: element d of a
+ * row is its E2M1 value times 2^(s - 127), s the E8M0 scale byte of group
+ * d / 32 (E2M1: sign, 2 exponent bits with bias 1, 1 fraction bit; exponent
+ * 0 gives 0 or 0.5; largest 6.  E8M0 255 is NaN).  The product is exact in
+ * the MFMA's float32 accumulation up to summation rounding; the result
+ * approximates the higher-precision score only as far as the encoding does.
+ *
+ * query        dtype MSA_DTYPE_MXFP4, [T, Hq, 64] bytes (128 elements, two per
+ *              byte, the even element in the low nibble), compact, 16-byte
+ *              aligned.
+ * query_scale  device uint8 [T, Hq, 4] compact: E8M0 of elements 32c..32c+31.
+ * key          dtype MSA_DTYPE_MXFP4, layouts as msa_index_score with a last
+ *              axis of 64 bytes: TND [T2, Hkv, 64], BBND [NP, 128, Hkv, 64],
+ *              BNBD [NP, Hkv, 128, 64]; paged dim0 stride any multiple of 16
+ *              bytes.
+ * key_scale    device uint8, compact, the key's layout with a last axis of 4:
+ *              TND [T2, Hkv, 4], BBND [NP, 128, Hkv, 4], BNBD [NP, Hkv, 128, 4],
+ *              indexed by page number (whatever the key's dim0 stride);
+ *              4-byte aligned, like query_scale.
+ * local_mode   msa_local_mode_t.  Everything else as msa_index_score.
+ *
+ * It always runs on the prefill tiles.  Returns as msa_index_score, plus
+ * MSA_ERR_DTYPE unless query and key are MSA_DTYPE_MXFP4 and MSA_ERR_NULL
+ * for a NULL scale.  (msa_index_score and its variants return MSA_ERR_SCALE
+ * for MXFP4 tensors: they cannot carry the group scales.) */
+msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* query_scale,
+                                   const msa_tensor_t* key, const uint8_t* key_scale,
+                                   const int32_t* start_loc, const int32_t* block_table,
+                                   int64_t max_blocks, const int32_t* cu_seqlens_q,
+                                   const int32_t* kv_len, int32_t batch, int32_t layout,
+                                   int32_t sparse_mode, int32_t init_blocks,
+                                   int32_t local_blocks, int32_t local_mode, float* out,
+                                   int64_t out_width, void* stream);
 
 /* Top-k block selection on the score rows: the stage the pages place after
  * the block score (the notes "MiniMax Sparse Attention: paper algorithm and

@@ -224,6 +224,36 @@ def test_local_mode_rules():
     assert call(cu=None, local_mode=1) == NULL
 
 
+def mx_call(q=None, k=None, *, qs=FAKE, ks=FAKE, start=FAKE, table=FAKE, mb=2, cu=FAKE,
+            kv=FAKE, B=1, layout=1, mode=3, init=0, local=1, local_mode=0, out=FAKE, width=16):
+    lib = m.load_library()
+    q = q if q is not None else tdesc([32, 8, 64], dtype=5)
+    k = k if k is not None else tdesc([8, 128, 1, 64], dtype=5)
+    return lib.msa_index_score_mxfp4(ctypes.byref(q), qs, ctypes.byref(k), ks, start, table, mb,
+                                     cu, kv, B, layout, mode, init, local, local_mode, out,
+                                     width, None)
+
+
+def test_mxfp4_rules():
+    q0 = tdesc([0, 8, 64], dtype=5)
+    assert mx_call(q=q0) == OK
+    assert mx_call(q=q0, k=tdesc([300, 1, 64], dtype=5), layout=0, table=None, mb=3) == OK
+    assert mx_call(qs=None) == NULL                                   # scales are required
+    assert mx_call(ks=None) == NULL
+    assert mx_call(q=tdesc([4, 8, 128], dtype=0)) == DTYPE            # not MXFP4
+    assert mx_call(k=tdesc([8, 128, 1, 128], dtype=1)) == DTYPE
+    assert mx_call(q=tdesc([4, 8, 128], dtype=5)) == SHAPE            # 64 bytes per row
+    assert mx_call(k=tdesc([8, 128, 1, 128], dtype=5)) == SHAPE
+    assert mx_call(qs=FAKE + 2) == STRIDE                             # 4-byte aligned scales
+    assert mx_call(ks=FAKE + 1) == STRIDE
+    assert mx_call(local_mode=3) == ATTR
+    assert mx_call(mode=1) == ATTR
+    # the other entries cannot carry the group scales
+    assert call(q=tdesc([4, 8, 64], dtype=5), k=tdesc([8, 128, 1, 64], dtype=5)) == SCALE
+    assert call(q=tdesc([4, 8, 64], dtype=5), k=tdesc([8, 128, 1, 64], dtype=5),
+                local_mode=1) == SCALE
+
+
 def test_block_topk_validation_without_launch():
     # Every call below fails validation or has no rows, so nothing launches.
     f = m.load_library().msa_block_topk

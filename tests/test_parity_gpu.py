@@ -42,18 +42,29 @@ def to_device(case, dev):
     ks = case.key_storage.to(dev)
     key = ks[:: case.gap + 1] if (case.gap and case.layout != "TND") else ks
     assert key.stride() == case.key.stride()
+    mx = lambda t: None if t is None else t.to(dev)   # noqa: E731
     return dict(
         query=case.query.to(dev), key=key, start_loc=case.start_loc.to(dev),
         block_table=None if case.block_table is None else case.block_table.to(dev),
         scale=None if case.scale is None else case.scale.to(dev),
-        cu_seqlens_q=case.cu_seqlens_q.to(dev), kv_len=case.kv_len.to(dev))
+        cu_seqlens_q=case.cu_seqlens_q.to(dev), kv_len=case.kv_len.to(dev),
+        q_mx=mx(case.q_mx_scale), k_mx=mx(case.k_mx_scale))
 
 
 def run_gpu(case, dev, family=-1):
+    """The GPU output of a case through the C ABI (MXFP4 cases take their own
+    entry, which always runs the prefill tiles, whatever ``family`` says)."""
     import block_max_qk_amd as m
     d = to_device(case, dev)
     W = m.msa_index_score_out_width(case.max_blocks)
     out = torch.full((case.Hq, case.T, W), 12345.0, dtype=torch.float32, device=dev)
+    if case.q_mx_scale is not None:
+        m.msa_index_score_mxfp4(d["query"], d["q_mx"], d["key"], d["k_mx"], d["start_loc"],
+                                d["block_table"], d["cu_seqlens_q"], d["kv_len"], case.layout,
+                                case.sparse_mode, case.init_blocks, case.local_blocks, out,
+                                case.max_blocks, local_mode=case.local_mode)
+        torch.cuda.synchronize()
+        return out.cpu()
     m.msa_index_score(d["query"], d["key"], d["start_loc"], d["block_table"], d["scale"],
                       d["cu_seqlens_q"], d["kv_len"], case.layout, case.sparse_mode,
                       case.init_blocks, case.local_blocks, out, case.max_blocks, family=family,
