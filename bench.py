@@ -19,6 +19,10 @@ workload instead (for measurement; the default line is the headline).
 chosen workload's score rows instead, with its own roofline (HBM bytes: every
 row's num_valid scores read, its k indices written).  ``--local-mode query``
 runs the workload with the local_mask window at each token's own block.
+``--config mx`` (or one of ``decode_bbnd_mxfp4``, ``prefill_tnd_mxfp4``,
+``prefill_bbnd_mxfp4``) measures the MXFP4 variants of three workloads
+(msa_index_score_mxfp4; roofline against FP4's 10.1 PFLOP/s dense peak, or
+HBM for the decode batch).
 """
 from __future__ import annotations
 
@@ -35,8 +39,9 @@ if ROOT not in sys.path:
 
 METRIC = ("block scores/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill), 1 GPU")
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 2500.0, "f8e4m3": 5000.0, "f8e5m2": 5000.0}
-ESIZE = {"f16": 2, "bf16": 2, "i8": 1, "f8e4m3": 1, "f8e5m2": 1}
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "i8": 2500.0, "f8e4m3": 5000.0, "f8e5m2": 5000.0,
+               "mxfp4": 10100.0}
+ESIZE = {"f16": 2, "bf16": 2, "i8": 1, "f8e4m3": 1, "f8e5m2": 1, "mxfp4": 0.5}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -74,13 +79,17 @@ def workload_stats(case) -> dict:
         visible += int((lim + 1).sum()) * case.Hq
         lmax = int(lim.max())
         if lmax >= 0:
-            k_bytes += (lmax + 1) * case.Hkv * case.D * esz      # each visible key read once
+            k_bytes += int((lmax + 1) * case.Hkv * case.D * esz)  # each visible key read once
             if case.scale is not None:
                 k_bytes += (lmax + 1) * case.Hkv * 4
+            if case.k_mx_scale is not None:                        # E8M0 per 32 elements
+                k_bytes += (lmax + 1) * case.Hkv * (case.D // 32)
             if case.layout != "TND":
                 table_bytes += (lmax // P + 1) * 4
     W = ((max(case.max_blocks, 1) + 15) // 16) * 16
     q_bytes = case.query.numel() * case.query.element_size()
+    if case.q_mx_scale is not None:
+        q_bytes += case.q_mx_scale.numel()
     out_bytes = case.Hq * case.T * W * 4
     return {"scores": scores, "out_entries": case.Hq * case.T * W,
             "flops": 2 * case.D * visible,
@@ -99,7 +108,10 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
 
     dev = torch.device("cuda:0")
     t_gen = time.time()
-    case = synth.config_case(c_idx)
+    nbase = len(synth.CONFIG_NAMES)
+    case = (synth.config_case(c_idx) if c_idx < nbase
+            else synth.mx_config_case(synth.MX_CONFIG_NAMES[c_idx - nbase]))
+    mx = case.q_mx_scale is not None
     if local_mode:
         case = dataclasses.replace(case, local_mode=local_mode)
     t_gen = time.time() - t_gen
@@ -107,15 +119,19 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     kname = case.key_dtype_name()
     is_decode = m.msa_index_score_kernel_family(case.T, case.batch, case.Hq, case.Hkv) == 0 \
         if family < 0 else family == 0
+    # (MXFP4 always runs the prefill tiles; a decode-shaped MXFP4 workload is
+    # still measured against HBM, its bound)
 
     # inputs resident in HBM; the key cache (and scale) replicated `copies` times
     W = m.msa_index_score_out_width(case.max_blocks)
     q = case.query.to(dev)
-    keys, scales = [], []
+    keys, scales, kmx = [], [], []
     for _ in range(copies):
         ks = case.key_storage.to(dev)
         keys.append(ks[:: case.gap + 1] if case.gap else ks)
         scales.append(None if case.scale is None else case.scale.to(dev))
+        kmx.append(None if case.k_mx_scale is None else case.k_mx_scale.to(dev))
+    qmx = None if case.q_mx_scale is None else case.q_mx_scale.to(dev)
     sl = case.start_loc.to(dev)
     bt = None if case.block_table is None else case.block_table.to(dev)
     cu = case.cu_seqlens_q.to(dev)
@@ -130,6 +146,17 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     for i in range(copies):
         qd, kd = describe(q), describe(keys[i])
         keep += [qd, kd]
+        if mx:
+            calls.append((ctypes.byref(qd), ctypes.c_void_p(qmx.data_ptr()), ctypes.byref(kd),
+                          ctypes.c_void_p(kmx[i].data_ptr()), ctypes.c_void_p(sl.data_ptr()),
+                          None if bt is None else ctypes.c_void_p(bt.data_ptr()),
+                          case.max_blocks, ctypes.c_void_p(cu.data_ptr()),
+                          ctypes.c_void_p(kv.data_ptr()), case.batch,
+                          m._binding.LAYOUT_CODE[case.layout], case.sparse_mode,
+                          case.init_blocks, case.local_blocks, case.local_mode,
+                          ctypes.c_void_p(out.data_ptr()), W,
+                          ctypes.c_void_p(stream.cuda_stream)))
+            continue
         a = (ctypes.byref(qd), ctypes.byref(kd), ctypes.c_void_p(sl.data_ptr()),
              None if bt is None else ctypes.c_void_p(bt.data_ptr()), case.max_blocks,
              None if scales[i] is None else ctypes.c_void_p(scales[i].data_ptr()),
@@ -138,7 +165,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
              case.local_blocks, case.local_mode, ctypes.c_void_p(out.data_ptr()), W,
              ctypes.c_void_p(stream.cuda_stream), family)
         calls.append(a)
-    fn = lib.msa_index_score_ex
+    fn = lib.msa_index_score_mxfp4 if mx else lib.msa_index_score_ex
 
     def step(i):
         st = fn(*calls[i % copies])
@@ -174,7 +201,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                 "frac": round(tflops / pk, 4)}
     # counters were taken with the per-request window (same memory accesses)
     roof["traffic"] = measured_traffic(case.name) if case.local_mode == 0 else None
-    roof["kernel"] = ("decode_kernel" if is_decode else "prefill_kernel") + f"<{kname}>"
+    roof["kernel"] = ("decode_kernel" if is_decode and not mx else "prefill_kernel") + f"<{kname}>"
     roof["kernel_ms_avg"] = round(kernel_ms, 5)
     roof["gpu_ms_per_step_span"] = round(span_ms, 5)
     roof["kernel_ms_median"] = round(kms[len(kms) // 2], 5)
@@ -193,8 +220,8 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                    "key_dtype": kname, "sparse_mode": case.sparse_mode,
                    "init_blocks": case.init_blocks, "local_blocks": case.local_blocks,
                    "local_window": "per-query" if case.local_mode else "per-request",
-                   "key_cache_copies": copies, "kernel_family": "decode" if is_decode
-                   else "prefill"},
+                   "key_cache_copies": copies,
+                   "kernel_family": "decode" if is_decode and not mx else "prefill"},
         "hbm_gbs": round(gbs, 1), "mfma_tflops": round(tflops, 3),
         "block_scores_per_step": stats["scores"], "out_entries_per_step": stats["out_entries"],
         "roofline": roof,
@@ -334,7 +361,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_bbnd_bf16",
-                    help="workload name, index 0-4, or 'all'")
+                    help="workload name or index, 'all' (the five base workloads) or 'mx' "
+                         "(their MXFP4 variants)")
     ap.add_argument("--copies", type=int, default=0,
                     help="key-cache copies to rotate over (0: enough to exceed 1 GiB)")
     ap.add_argument("--family", type=int, default=-1, help="-1 auto, 0 decode, 1 prefill tiles")
@@ -375,21 +403,26 @@ def main():
         return
 
     import synth
-    names = list(synth.CONFIG_NAMES)
+    names = list(synth.CONFIG_NAMES) + list(synth.MX_CONFIG_NAMES)
     if args.config == "all":
-        todo = list(range(len(names)))
+        todo = list(range(len(synth.CONFIG_NAMES)))
+    elif args.config == "mx":
+        todo = list(range(len(synth.CONFIG_NAMES), len(names)))
     elif args.config.isdigit():
         todo = [int(args.config)]
     else:
         todo = [names.index(args.config)]
     for c in todo:
+        if args.topk and c >= len(synth.CONFIG_NAMES):
+            print("--topk runs on the five base workloads", file=sys.stderr)
+            sys.exit(2)
         if args.topk:
             print(json.dumps(bench_topk(c, args.steps, args.warmup, not args.no_cpu_baseline,
                                         args)), flush=True)
             continue
         copies = args.copies
         if copies <= 0:
-            copies = 4 if c in (1, 3) else 1
+            copies = 4 if names[c].startswith("decode") else 1
         r = bench_config(c, args.steps, args.warmup, copies, args.family,
                          not args.no_cpu_baseline, args,
                          local_mode=1 if args.local_mode == "query" else 0)

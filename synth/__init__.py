@@ -9,7 +9,9 @@ and benchmark can use it without sharing any scoring code.
 from .inputs import (  # noqa: F401
     MsaCase,
     CONFIG_NAMES,
+    MX_CONFIG_NAMES,
     config_case,
+    mx_config_case,
     make_case,
     edge_cases,
     random_cases,

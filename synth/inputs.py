@@ -342,6 +342,30 @@ def config_case(c: int) -> MsaCase:
     raise IndexError(c)
 
 
+# The MXFP4 variants of three workloads: the same shapes, lengths and tables,
+# with MXFP4 query and key (N(0,1) encoded per 32-element group).
+MX_CONFIG_NAMES = ("decode_bbnd_mxfp4", "prefill_tnd_mxfp4", "prefill_bbnd_mxfp4")
+_MX_OF = {"decode_bbnd_mxfp4": 1, "prefill_tnd_mxfp4": 2, "prefill_bbnd_mxfp4": 4}
+
+
+def mx_config_case(name: str) -> MsaCase:
+    c = _MX_OF[name]
+    seed = 20261300 + c + 1
+    if c == 1:
+        return make_case(name, seed, q_lens=[1], kv_lens=None, kv_len_draw=(1, 32768), B=64,
+                         Hq=16, Hkv=1, qdtype="mxfp4", layout="BBND", MB=256, NP=16384,
+                         table="perm", sparse_mode=3, init_blocks=0, local_blocks=1)
+    if c == 2:
+        q_lens = [1024, 2048, 4096, 8192]
+        prefix = [0, 4096, 16384, 57344]
+        kv = [p + q for p, q in zip(prefix, q_lens)]
+        return make_case(name, seed, q_lens=q_lens, kv_lens=kv, Hq=32, Hkv=4, qdtype="mxfp4",
+                         layout="TND", sparse_mode=3, init_blocks=1, local_blocks=2)
+    return make_case(name, seed, q_lens=[4096], kv_lens=[131072], Hq=64, Hkv=8,
+                     qdtype="mxfp4", layout="BBND", MB=1024, NP=1024, table="perm",
+                     sparse_mode=3, init_blocks=1, local_blocks=4)
+
+
 # ---------------------------------------------------------------------------
 # poisoning of bytes the operator must never let into a result
 # ---------------------------------------------------------------------------

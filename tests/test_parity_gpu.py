@@ -199,3 +199,28 @@ def test_full_size_per_query_local_window(c_idx, dev):
         pos = int(kv[b]) - (t1 - t0) + torch.arange(t1 - t0)
         own = got[:, t0:t1].gather(2, (pos // 128).clamp(min=0)[None, :, None].expand(c.Hq, -1, 1))
         assert bool((own[:, pos >= 0] == 1e29).all()), c.name
+
+
+
+@pytest.mark.parametrize("name", ["decode_bbnd_mxfp4", "prefill_bbnd_mxfp4"])
+def test_full_size_mxfp4(name, dev):
+    # The MXFP4 variants at their measured sizes: the whole decode batch, and
+    # sampled rows and entries of the chunked prefill.
+    c = synth.mx_config_case(name)
+    log(f"[gpu] config {c.name}")
+    got = run_gpu(c, dev)
+    if name.startswith("decode"):
+        r = check(oracle_out(c), got, tol_of(c))
+        log(f"[gpu] {c.name} full: {r}")
+        assert r["ok"], r
+        return
+    pts, nrows = _sample_points(c, got.shape, 32, 10000, 333)
+    ref = oracle.index_score_case_points(c, pts)
+    gv = got[pts[:, 0], pts[:, 1], pts[:, 2]]
+    W = got.shape[2]
+    nfull = nrows * W
+    r = check(ref[:nfull].reshape(nrows, W), gv[:nfull].reshape(nrows, W), tol_of(c))
+    log(f"[gpu] {c.name} sampled rows: {r}")
+    assert r["ok"], r
+    r2 = compare_values(ref[nfull:], gv[nfull:], tol_of(c))
+    assert r2["ok"], r2
