@@ -8,8 +8,9 @@ head, kv_len ~ U[1, 32768], bf16 keys in 16384 paged 128-token blocks
 (BBND) behind a random block table, right-down causal, local_blocks = 1.
 
 Timed region: W untimed warmup steps, then exactly K steps bracketed by
-torch.cuda.synchronize(); every launch is also bracketed by HIP events on the
-launch stream, which give the kernel's average duration for the roofline.
+torch.cuda.synchronize(); one pair of HIP events on the launch stream around
+the K launches (nothing recorded between them) gives the kernel's average
+duration for the roofline.
 To keep the 256 MB Infinity Cache from serving repeated reads, the key cache
 is replicated into several HBM copies and the steps rotate over them.
 
@@ -175,19 +176,20 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # one HIP event pair around the K launches on the launch stream, nothing
+    # between them: the average launch duration (events between launches add
+    # their own processing time to each)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev0[i].record(stream)
         step(i)
-        ev1[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
-    kernel_ms = sum(kms) / len(kms)
-    span_ms = ev0[0].elapsed_time(ev1[steps - 1]) / steps
+    kernel_ms = e0.elapsed_time(e1) / steps
     ms_per_step = (t1 - t0) * 1e3 / steps
 
     gbs = stats["bytes"] / (kernel_ms * 1e-3) / 1e9
@@ -203,8 +205,6 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     roof["traffic"] = measured_traffic(case.name) if case.local_mode == 0 else None
     roof["kernel"] = ("decode_kernel" if is_decode and not mx else "prefill_kernel") + f"<{kname}>"
     roof["kernel_ms_avg"] = round(kernel_ms, 5)
-    roof["gpu_ms_per_step_span"] = round(span_ms, 5)
-    roof["kernel_ms_median"] = round(kms[len(kms) // 2], 5)
     roof["algorithmic_bytes"] = stats["bytes"]
     roof["algorithmic_flops"] = stats["flops"]
 
@@ -311,17 +311,16 @@ def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) ->
     for _ in range(warmup):
         m.msa_block_topk(scores, nv, k, out, stream=stream)
     torch.cuda.synchronize()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev0[i].record(stream)
         m.msa_block_topk(scores, nv, k, out, stream=stream)
-        ev1[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kms = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
-    kernel_ms = sum(kms) / len(kms)
+    kernel_ms = e0.elapsed_time(e1) / steps
     ms_per_step = (t1 - t0) * 1e3 / steps
     alg = rows * (nv + k) * 4      # each row's num_valid scores read, k indices written
     gbs = alg / (kernel_ms * 1e-3) / 1e9
@@ -333,9 +332,9 @@ def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) ->
         "config": {"workload": case.name, "stage": "top-k", "k": k, "rows": rows,
                    "width": W, "num_valid": nv},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("topk:" + case.name),
                      "kernel": "topk_kernel", "kernel_ms_avg": round(kernel_ms, 5),
-                     "kernel_ms_median": round(kms[len(kms) // 2], 5),
                      "algorithmic_bytes": alg},
         "cpu_baseline": None,
     }
