@@ -18,7 +18,12 @@ constexpr int kP = 128;   // tokens per logical block
 constexpr int kD = 128;   // index head dimension
 
 // Element kinds of the key (the query kind follows from it).
-enum KeyKind : int { KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4, KMXFP4 = 5 };
+// MXFP4 has two prefill instantiations: KMXFP4 with four 32-row N tiles per
+// wave, KMXFP4_N2 with two (short query runs, where the 512-row tile would
+// mostly be empty).
+enum KeyKind : int {
+  KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4, KMXFP4 = 5, KMXFP4_N2 = 6
+};
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -339,7 +344,7 @@ template <int KK>
 struct Kind {
   static constexpr bool is_f8 = (KK == KF8E4M3 || KK == KF8E5M2);
   static constexpr bool is_i8 = (KK == KI8);
-  static constexpr bool is_fp4 = (KK == KMXFP4);
+  static constexpr bool is_fp4 = (KK == KMXFP4 || KK == KMXFP4_N2);
   static constexpr int q_bytes = is_f8 ? 1 : 2;   // query element size (not MXFP4)
   static constexpr int k_bytes = (is_f8 || is_i8) ? 1 : 2;
   static constexpr int q_row = is_fp4 ? kD / 2 : kD * q_bytes;   // bytes per query row

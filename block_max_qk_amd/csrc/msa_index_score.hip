@@ -208,7 +208,9 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   // plan
   const int32_t g = (int32_t)(Hq / Hkv);
   const int fam = is_mx ? 1 : family >= 0 ? family : choose_family(T, batch, g);
-  const int rows = fam == 1 ? msa::prefill_rows(is_mx ? msa::KMXFP4 : key->dtype)
+  // MXFP4: four N tiles per wave for long query runs, two for short ones
+  const int mx_kind = choose_family(T, batch, g) == 1 ? msa::KMXFP4 : msa::KMXFP4_N2;
+  const int rows = fam == 1 ? msa::prefill_rows(is_mx ? mx_kind : key->dtype)
                             : msa::kDecodeRows;
   Params p{};
   p.q = static_cast<const uint8_t*>(query->data);
@@ -281,8 +283,12 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
     case MSA_DTYPE_I8: e = launch<msa::KI8>(fam, p, grid, s); break;
     case MSA_DTYPE_F8E4M3: e = launch<msa::KF8E4M3>(fam, p, grid, s); break;
     case MSA_DTYPE_MXFP4:
-      hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4>, dim3((unsigned)grid), dim3(256), 0, s,
-                         p);
+      if (mx_kind == msa::KMXFP4)
+        hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4>, dim3((unsigned)grid), dim3(256), 0,
+                           s, p);
+      else
+        hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4_N2>, dim3((unsigned)grid), dim3(256),
+                           0, s, p);
       e = hipGetLastError();
       break;
     default: e = launch<msa::KF8E5M2>(fam, p, grid, s); break;

@@ -40,7 +40,9 @@ constexpr int kPrefillChunk = 16;   // blocks per prefill work item (fp8: twice 
 // waves of them.  More N tiles let one key fragment read from LDS feed more
 // MFMAs, at the cost of query registers (and so waves per SIMD): 16-bit keys
 // take three (two waves per SIMD), fp8 and int8 two.
-constexpr int prefill_ntw(int kk) { return (kk == KF16 || kk == KBF16) ? 3 : 2; }
+constexpr int prefill_ntw(int kk) {
+  return (kk == KF16 || kk == KBF16) ? 3 : kk == KMXFP4 ? 4 : 2;
+}
 constexpr int prefill_rows(int kk) { return 4 * 32 * prefill_ntw(kk); }
 
 // ---------------------------------------------------------------------------
