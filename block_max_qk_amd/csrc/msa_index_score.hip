@@ -261,12 +261,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hchunks = (g + p.hpt - 1) / p.hpt;
   // prefill units: (KV head, head chunk, block chunk); decode units: (KV
   // head, head chunk), each walking its own copy of the batch's work list
-  // fp8 prefill amortises each work item's query tile and set-up over more
-  // blocks (measured faster); 16-bit keys balance better with 16
-  p.chunk = (fam == 1 && (key->dtype == MSA_DTYPE_F8E4M3 || key->dtype == MSA_DTYPE_F8E5M2 ||
-                          is_mx))
-                ? 2 * msa::kPrefillChunk
-                : msa::kPrefillChunk;
+  p.chunk = msa::kPrefillChunk;
   p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
   p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
