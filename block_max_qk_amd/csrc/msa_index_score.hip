@@ -261,7 +261,10 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hchunks = (g + p.hpt - 1) / p.hpt;
   // prefill units: (KV head, head chunk, block chunk); decode units: (KV
   // head, head chunk), each walking its own copy of the batch's work list
-  p.chunk = msa::kPrefillChunk;
+  // (MXFP4 on short query runs: 8-block work items, whose chains of
+  // dependent block stages are short enough to keep the copies of many in
+  // flight -- 48.6 -> 37.0 us on the decode batch; 4 measured 40.6 us)
+  p.chunk = (is_mx && mx_kind == msa::KMXFP4_N2) ? 8 : msa::kPrefillChunk;
   p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
   p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
