@@ -18,12 +18,7 @@ constexpr int kP = 128;   // tokens per logical block
 constexpr int kD = 128;   // index head dimension
 
 // Element kinds of the key (the query kind follows from it).
-// MXFP4 has two prefill instantiations: KMXFP4 with four 32-row N tiles per
-// wave, KMXFP4_N2 with two (short query runs, where the 512-row tile would
-// mostly be empty).
-enum KeyKind : int {
-  KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4, KMXFP4 = 5, KMXFP4_N2 = 6
-};
+enum KeyKind : int { KF16 = 0, KBF16 = 1, KI8 = 2, KF8E4M3 = 3, KF8E5M2 = 4, KMXFP4 = 5 };
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -340,11 +335,20 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp4(i32x4 a, i32x4 b, f32x16 c, i
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
 }
 
+// The 16x16x128 form: lane l covers row l % 16 and the 32 elements
+// 32 (l / 16) + [0, 32) of the 128-deep product (16 bytes), scale byte 0 of
+// sa / sb; lane l's result is column l % 16, rows 4 (l / 16) + [0, 4).
+__device__ __forceinline__ f32x4 mfma16x16x128_fp4(i32x4 a, i32x4 b, f32x4 c, int sa, int sb) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+
 template <int KK>
 struct Kind {
   static constexpr bool is_f8 = (KK == KF8E4M3 || KK == KF8E5M2);
   static constexpr bool is_i8 = (KK == KI8);
-  static constexpr bool is_fp4 = (KK == KMXFP4 || KK == KMXFP4_N2);
+  static constexpr bool is_fp4 = (KK == KMXFP4);
   static constexpr int q_bytes = is_f8 ? 1 : 2;   // query element size (not MXFP4)
   static constexpr int k_bytes = (is_f8 || is_i8) ? 1 : 2;
   static constexpr int q_row = is_fp4 ? kD / 2 : kD * q_bytes;   // bytes per query row

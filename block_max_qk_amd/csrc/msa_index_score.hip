@@ -189,7 +189,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (init_blocks < 0 || local_blocks < 0 || init_blocks > limit || local_blocks > limit)
     return MSA_ERR_ATTR;
   if (family < -1 || family > 1) return MSA_ERR_ATTR;
-  if (is_mx && family == 0) return MSA_ERR_ATTR;   // MXFP4 runs on the prefill tiles only
+  if (is_mx && family == 0) return MSA_ERR_ATTR;   // MXFP4 picks its kernel itself
   if (local_mode != MSA_LOCAL_PER_REQUEST && local_mode != MSA_LOCAL_PER_QUERY)
     return MSA_ERR_ATTR;
 
@@ -207,10 +207,11 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
 
   // plan
   const int32_t g = (int32_t)(Hq / Hkv);
-  const int fam = is_mx ? 1 : family >= 0 ? family : choose_family(T, batch, g);
-  // MXFP4: four N tiles per wave for long query runs, two for short ones
-  const int mx_kind = choose_family(T, batch, g) == 1 ? msa::KMXFP4 : msa::KMXFP4_N2;
-  const int rows = fam == 1 ? msa::prefill_rows(is_mx ? mx_kind : key->dtype)
+  // MXFP4: the prefill tiles for long query runs, its own decode kernel
+  // (16-row tiles over ranges of blocks) for short ones
+  const bool mx_short = is_mx && choose_family(T, batch, g) == 0;
+  const int fam = is_mx ? (mx_short ? 0 : 1) : family >= 0 ? family : choose_family(T, batch, g);
+  const int rows = fam == 1 ? msa::prefill_rows(is_mx ? msa::KMXFP4 : key->dtype)
                             : msa::kDecodeRows;
   Params p{};
   p.q = static_cast<const uint8_t*>(query->data);
@@ -261,11 +262,8 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hchunks = (g + p.hpt - 1) / p.hpt;
   // prefill units: (KV head, head chunk, block chunk); decode units: (KV
   // head, head chunk), each walking its own copy of the batch's work list
-  // (MXFP4 on short query runs: 8-block work items, whose chains of
-  // dependent block stages are short enough to keep the copies of many in
-  // flight -- 48.6 -> 37.0 us on the decode batch; 4 measured 40.6 us)
-  p.chunk = (is_mx && mx_kind == msa::KMXFP4_N2) ? 8 : msa::kPrefillChunk;
-  p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
+  p.chunk = mx_short ? msa::kMxDecodeChunk : msa::kPrefillChunk;
+  p.nchunks = (fam == 1 || mx_short) ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
   p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
   p.ntiles = (int32_t)std::min<int64_t>(T, bound);
@@ -281,12 +279,11 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
     case MSA_DTYPE_I8: e = launch<msa::KI8>(fam, p, grid, s); break;
     case MSA_DTYPE_F8E4M3: e = launch<msa::KF8E4M3>(fam, p, grid, s); break;
     case MSA_DTYPE_MXFP4:
-      if (mx_kind == msa::KMXFP4)
+      if (mx_short)
+        hipLaunchKernelGGL(msa::decode_mx_kernel, dim3((unsigned)grid), dim3(64), 0, s, p);
+      else
         hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4>, dim3((unsigned)grid), dim3(256), 0,
                            s, p);
-      else
-        hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4_N2>, dim3((unsigned)grid), dim3(256),
-                           0, s, p);
       e = hipGetLastError();
       break;
     default: e = launch<msa::KF8E5M2>(fam, p, grid, s); break;

@@ -907,4 +907,138 @@ void prefill_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 on short query runs (decode batches): one wave per work item of
+// `locate` -- a 16-row tile (hpt heads x tpt tokens of one KV group) over a
+// range of kMxDecodeChunk blocks.  Each 16-token sub-tile of a key block is
+// one MFMA 16x16x128 (the whole 128-deep row): key tokens on the M side,
+// query rows on the N side.  Lane l loads 16 bytes of token l % 16 (group
+// l / 16), so the 64 lanes of one load read 16 whole 64-byte token rows, and
+// the token's scale word; the next block's loads are issued before the
+// current block's product.  HBM-bound: every visible key byte is read once.
+// ---------------------------------------------------------------------------
+constexpr int kMxDecodeChunk = 8;
+
+__global__ __launch_bounds__(64) void decode_mx_kernel(Params p) {
+  const Work w = locate(p);
+  if (!w.valid) return;
+  const int l = lane_id();
+  const int n = l & 15;          // key token of a sub-tile (A) / query row (B and results)
+  const int G = l >> 4;          // 32-element group of the row
+  const int i0 = w.t0 - p.cu_q[w.b];
+  const int ti = n / p.hpt;
+  const int hg = w.hc * p.hpt + (n - ti * p.hpt);
+  const bool row_ok = n < p.hpt * p.tpt && ti < w.ntok && hg < p.g;
+  const int lim = (row_ok && w.L > 0) ? last_visible(p, w, i0 + ti) : -1;
+  const bool tile_ok = w.L > 0 && w.ntok > 0;
+  const int lim_lo = __builtin_amdgcn_readfirstlane(tile_ok ? last_visible(p, w, i0) : -1);
+  const int lim_hi = tile_ok ? last_visible(p, w, i0 + w.ntok - 1) : -1;
+  const int nb = min((w.L + kP - 1) / kP, p.MB);
+  // the block loop's bounds are the same on every lane; readfirstlane puts
+  // them in scalar registers, so that the loop is not compiled as a divergent
+  // one (whose merged wait counts would stall on the loads in flight)
+  const int vend = __builtin_amdgcn_readfirstlane(
+      max(w.c0, min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0)));
+  const int c0 = __builtin_amdgcn_readfirstlane(w.c0);
+  const int anchor = local_anchor(p, w, i0 + ti);
+  float* const orow =
+      p.out + (((int64_t)w.hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W;
+
+  // query row n, group G (B operand) and its scale byte
+  i32x4 qv = i32x4{0, 0, 0, 0};
+  int qs = 127;
+  if (row_ok && c0 < vend) {
+    const int64_t qrow = (int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg);
+    qv = ld16(p.q + qrow * (kD / 2) + 16 * G);
+    qs = p.q_mx[qrow * (kD / 32) + G];
+  }
+
+  // page indices of the work item's blocks, one per lane, read with readlane
+  // (a table read inside the loop would wait for the key loads in flight)
+  int pidx = 0;
+  if (p.paged && l < vend - c0) pidx = p.block_table[(int64_t)w.b * p.MB + c0 + l];
+
+  // a block's eight A fragments (16 bytes of token 16 s + n) and those
+  // tokens' scale words; rows past kv_len read row 0 (masked later)
+  auto load = [&](int beta, i32x4 (&a)[8], uint32_t (&sc)[8]) {
+    int64_t kb, sb;
+    if (p.paged) {
+      const int64_t page = __builtin_amdgcn_readlane(pidx, beta - c0);
+      kb = page * p.k_page_stride;
+      sb = page * p.mx_page_stride;
+    } else {
+      kb = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
+      sb = (w.koff + (int64_t)beta * kP) * p.mx_row_stride;
+    }
+    const uint8_t* kp = p.k + uniform64(kb + (int64_t)w.hk * p.k_head_stride);
+    const uint8_t* sp = p.k_mx + uniform64(sb + (int64_t)w.hk * p.mx_head_stride);
+    const int nvalid = min(kP, w.L - beta * kP);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int jj = 16 * s + n;
+      const int src = jj < nvalid ? jj : 0;
+      a[s] = ld16_stream(kp + (uint32_t)(src * p.k_row_stride + 16 * G));
+      sc[s] = *reinterpret_cast<const uint32_t*>(sp + (uint32_t)(src * p.mx_row_stride));
+    }
+  };
+
+  bool pend_ok = false;
+  float* pend_ptr = orow;
+  float pend_val = 0.f;
+  // one block's scores from its fragments, after the previous block's
+  // result is stored (the caller has issued the next block's loads first)
+  auto step = [&](int beta, const i32x4 (&ka)[8], const uint32_t (&sa)[8]) {
+    if (pend_ok) *pend_ptr = pend_val;
+    const bool full = beta * kP + kP - 1 <= lim_lo;
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f32x4 acc =
+          mfma16x16x128_fp4(ka[s], qv, f32x4{0.f, 0.f, 0.f, 0.f}, (sa[s] >> (8 * G)) & 255, qs);
+      // acc[k] is key token 16 s + 4 G + k of row n
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float v = acc[k];
+        if (!full) v = (beta * kP + 16 * s + 4 * G + k <= lim) ? v : -__builtin_inff();
+        m = fmaxf(m, v);
+      }
+    }
+    // the four groups hold disjoint tokens of the same row
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    pend_ok = G == 0 && row_ok;
+    pend_ptr = orow + beta;
+    pend_val = finish(p, w.L, anchor, beta, true, m);
+  };
+  // two register buffers used in turn, one block ahead (a copy between them
+  // would wait for the loads in flight); the loop has no exit between its
+  // two halves, which would make the compiler wait there as well
+  i32x4 fa[8], fb[8];
+  uint32_t ca[8], cb[8];
+  if (c0 < vend) {
+    load(c0, fa, ca);
+    int beta = c0;
+    for (; beta + 2 < vend; beta += 2) {
+      load(beta + 1, fb, cb);
+      step(beta, fa, ca);
+      load(beta + 2, fa, ca);
+      step(beta + 1, fb, cb);
+    }
+    if (beta + 1 < vend) {
+      load(beta + 1, fb, cb);
+      step(beta, fa, ca);
+      step(beta + 1, fb, cb);
+    } else {
+      step(beta, fa, ca);
+    }
+  }
+  if (pend_ok) *pend_ptr = pend_val;
+  // the work item's columns past the visible blocks: -inf and local_mask,
+  // four columns per row pass (lane group G takes columns G, G + 4, ...)
+  if (row_ok) {
+    for (int beta = vend + G; beta < w.c1; beta += 4)
+      orow[beta] = finish(p, w.L, anchor, beta, false, 0.f);
+  }
+}
+
 }  // namespace msa
