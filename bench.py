@@ -120,8 +120,6 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
     kname = case.key_dtype_name()
     is_decode = m.msa_index_score_kernel_family(case.T, case.batch, case.Hq, case.Hkv) == 0 \
         if family < 0 else family == 0
-    # (MXFP4 always runs the prefill tiles; a decode-shaped MXFP4 workload is
-    # still measured against HBM, its bound)
 
     # inputs resident in HBM; the key cache (and scale) replicated `copies` times
     W = m.msa_index_score_out_width(case.max_blocks)
@@ -203,7 +201,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                 "frac": round(tflops / pk, 4)}
     # counters were taken with the per-request window (same memory accesses)
     roof["traffic"] = measured_traffic(case.name) if case.local_mode == 0 else None
-    roof["kernel"] = ("decode_kernel" if is_decode and not mx else "prefill_kernel") + f"<{kname}>"
+    roof["kernel"] = ("decode_kernel" if is_decode else "prefill_kernel") + f"<{kname}>"
     roof["kernel_ms_avg"] = round(kernel_ms, 5)
     roof["algorithmic_bytes"] = stats["bytes"]
     roof["algorithmic_flops"] = stats["flops"]
@@ -221,7 +219,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                    "init_blocks": case.init_blocks, "local_blocks": case.local_blocks,
                    "local_window": "per-query" if case.local_mode else "per-request",
                    "key_cache_copies": copies,
-                   "kernel_family": "decode" if is_decode and not mx else "prefill"},
+                   "kernel_family": "decode" if is_decode else "prefill"},
         "hbm_gbs": round(gbs, 1), "mfma_tflops": round(tflops, 3),
         "block_scores_per_step": stats["scores"], "out_entries_per_step": stats["out_entries"],
         "roofline": roof,

@@ -30,7 +30,8 @@ LAYOUT_CODE = {"TND": 0, "BBND": 1, "BNBD": 2}
 STATUS_NAMES = ["MSA_OK", "MSA_ERR_NULL", "MSA_ERR_LAYOUT", "MSA_ERR_DTYPE", "MSA_ERR_SHAPE",
                 "MSA_ERR_STRIDE", "MSA_ERR_SCALE", "MSA_ERR_ATTR", "MSA_ERR_HIP"]
 EXPORTED = ("msa_index_score", "msa_index_score_family", "msa_index_score_ex",
-            "msa_index_score_mxfp4", "msa_index_score_out_width", "msa_status_str",
+            "msa_index_score_mxfp4", "msa_index_score_mxfp4_family",
+            "msa_index_score_out_width", "msa_status_str",
             "msa_index_score_kernel_family", "msa_block_topk")
 LOCAL_MODE_CODE = {"request": 0, "query": 1}
 
@@ -82,6 +83,9 @@ def load_library(path: Optional[str] = None):
             ctypes.c_int64, ptr, ptr, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ptr, ctypes.c_int64, ptr]
         lib.msa_index_score_mxfp4.restype = ctypes.c_int
+        lib.msa_index_score_mxfp4_family.argtypes = (lib.msa_index_score_mxfp4.argtypes +
+                                                     [ctypes.c_int32])
+        lib.msa_index_score_mxfp4_family.restype = ctypes.c_int
         lib.msa_index_score_out_width.argtypes = [ctypes.c_int64]
         lib.msa_index_score_out_width.restype = ctypes.c_int64
         lib.msa_status_str.argtypes = [ctypes.c_int32]
@@ -184,10 +188,12 @@ def msa_index_score_mxfp4(query: torch.Tensor, query_scale: torch.Tensor, key: t
                           block_table: Optional[torch.Tensor], cu_seqlens_q: torch.Tensor,
                           kv_len: torch.Tensor, layout, sparse_mode: int, init_blocks: int,
                           local_blocks: int, out: torch.Tensor, max_blocks: int, stream=None,
-                          local_mode=0) -> torch.Tensor:
+                          local_mode=0, family: int = -1) -> torch.Tensor:
     """The MXFP4 entry: ``query`` [T, Hq, 64] and ``key`` (layout-shaped, last
     axis 64) uint8 hold E2M1 pairs; ``query_scale`` [T, Hq, 4] and
-    ``key_scale`` (the key's layout with a last axis of 4) uint8 hold E8M0."""
+    ``key_scale`` (the key's layout with a last axis of 4) uint8 hold E8M0.
+    ``family`` -1 picks the kernel family from the sizes, 0/1 force the
+    decode/prefill tiles."""
     lib = load_library()
     dev = out.device
     for name, t in (("query", query), ("query_scale", query_scale), ("key", key),
@@ -211,12 +217,12 @@ def msa_index_score_mxfp4(query: torch.Tensor, query_scale: torch.Tensor, key: t
         stream = stream.cuda_stream
     lm = LOCAL_MODE_CODE.get(local_mode, -1) if isinstance(local_mode, str) else int(local_mode)
     qd, kd = describe(query), describe(key)
-    st = lib.msa_index_score_mxfp4(
+    st = lib.msa_index_score_mxfp4_family(
         ctypes.byref(qd), _ptr(query_scale), ctypes.byref(kd), _ptr(key_scale),
         _ptr(start_loc), _ptr(block_table), int(max_blocks), _ptr(cu_seqlens_q),
         _ptr(kv_len), int(kv_len.numel()), _layout_code(layout), int(sparse_mode),
         int(init_blocks), int(local_blocks), lm, _ptr(out), int(out.shape[2]),
-        ctypes.c_void_p(stream))
+        ctypes.c_void_p(stream), int(family))
     if st != 0:
         cls = MsaLayoutError if st == 2 else MsaError
         raise cls(st, msa_status_str(st))

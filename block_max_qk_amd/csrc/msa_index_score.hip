@@ -189,7 +189,6 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (init_blocks < 0 || local_blocks < 0 || init_blocks > limit || local_blocks > limit)
     return MSA_ERR_ATTR;
   if (family < -1 || family > 1) return MSA_ERR_ATTR;
-  if (is_mx && family == 0) return MSA_ERR_ATTR;   // MXFP4 picks its kernel itself
   if (local_mode != MSA_LOCAL_PER_REQUEST && local_mode != MSA_LOCAL_PER_QUERY)
     return MSA_ERR_ATTR;
 
@@ -207,10 +206,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
 
   // plan
   const int32_t g = (int32_t)(Hq / Hkv);
-  // MXFP4: the prefill tiles for long query runs, its own decode kernel
-  // (16-row tiles over ranges of blocks) for short ones
-  const bool mx_short = is_mx && choose_family(T, batch, g) == 0;
-  const int fam = is_mx ? (mx_short ? 0 : 1) : family >= 0 ? family : choose_family(T, batch, g);
+  const int fam = family >= 0 ? family : choose_family(T, batch, g);
   const int rows = fam == 1 ? msa::prefill_rows(is_mx ? msa::KMXFP4 : key->dtype)
                             : msa::kDecodeRows;
   Params p{};
@@ -262,8 +258,8 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hchunks = (g + p.hpt - 1) / p.hpt;
   // prefill units: (KV head, head chunk, block chunk); decode units: (KV
   // head, head chunk), each walking its own copy of the batch's work list
-  p.chunk = mx_short ? msa::kMxDecodeChunk : msa::kPrefillChunk;
-  p.nchunks = (fam == 1 || mx_short) ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
+  p.chunk = msa::kPrefillChunk;
+  p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
   p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
   p.ntiles = (int32_t)std::min<int64_t>(T, bound);
@@ -278,14 +274,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
     case MSA_DTYPE_BF16: e = launch<msa::KBF16>(fam, p, grid, s); break;
     case MSA_DTYPE_I8: e = launch<msa::KI8>(fam, p, grid, s); break;
     case MSA_DTYPE_F8E4M3: e = launch<msa::KF8E4M3>(fam, p, grid, s); break;
-    case MSA_DTYPE_MXFP4:
-      if (mx_short)
-        hipLaunchKernelGGL(msa::decode_mx_kernel, dim3((unsigned)grid), dim3(64), 0, s, p);
-      else
-        hipLaunchKernelGGL(msa::prefill_kernel<msa::KMXFP4>, dim3((unsigned)grid), dim3(256), 0,
-                           s, p);
-      e = hipGetLastError();
-      break;
+    case MSA_DTYPE_MXFP4: e = launch<msa::KMXFP4>(fam, p, grid, s); break;
     default: e = launch<msa::KF8E5M2>(fam, p, grid, s); break;
   }
   return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
@@ -392,6 +381,22 @@ msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* que
   return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
              cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
              local_mode, out, out_width, stream, -1);
+}
+
+msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8_t* query_scale,
+                                          const msa_tensor_t* key, const uint8_t* key_scale,
+                                          const int32_t* start_loc, const int32_t* block_table,
+                                          int64_t max_blocks, const int32_t* cu_seqlens_q,
+                                          const int32_t* kv_len, int32_t batch, int32_t layout,
+                                          int32_t sparse_mode, int32_t init_blocks,
+                                          int32_t local_blocks, int32_t local_mode, float* out,
+                                          int64_t out_width, void* stream, int32_t family) {
+  if (!query || !key) return MSA_ERR_NULL;
+  if (query->dtype != MSA_DTYPE_MXFP4 || key->dtype != MSA_DTYPE_MXFP4) return MSA_ERR_DTYPE;
+  if (!query_scale || !key_scale) return MSA_ERR_NULL;
+  return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
+             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
+             local_mode, out, out_width, stream, family);
 }
 
 int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }

@@ -60,6 +60,11 @@ constexpr int prefill_rows(int kk) { return 4 * 32 * prefill_ntw(kk); }
 // one round of workgroups (as many as the chip holds at once), so no
 // workgroup waits for a slot.  Columns a tile cannot see (past its last
 // visible block, up to the output width) are written by a fill pass.
+// Key blocks are loaded to registers: 16-bit, fp8 and int8 blocks pass
+// through a per-wave LDS area into the MFMA operand order; MXFP4 blocks
+// (8 KB) load straight into it and take four workgroups per CU instead of
+// two (measured: 8 KB blocks gain nothing from loading two to four of a
+// wave's blocks together at two workgroups per CU).
 // ---------------------------------------------------------------------------
 
 // Visible blocks of tile j of a request (kv_len L, L_q query tokens): up to
@@ -199,14 +204,17 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
 }
 
 template <int KK>
-__global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Params p) {
+__global__ __launch_bounds__(256, Kind<KK>::is_fp4 ? 4 : (Kind<KK>::is_i8 ? 3 : 2))
+void decode_kernel(Params p) {
   using Kd = Kind<KK>;
   // int8: each wave's current block of column scales, staged so that every
   // lane can read the four consecutive scales of its accumulator tokens
   __shared__ __attribute__((aligned(16))) float dscl[Kd::is_i8 ? 4 : 1][kP];
   // four transpose areas per wave, each one 16-token sub-tile of key rows
+  // (MXFP4 reads its operands straight from memory and uses none)
   constexpr int RBY = kD * Kd::k_bytes;        // key row bytes
-  __shared__ __attribute__((aligned(16))) uint8_t dkt[4][4][16 * RBY];
+  __shared__ __attribute__((aligned(16))) uint8_t dkt[Kd::is_fp4 ? 1 : 4][Kd::is_fp4 ? 1 : 4]
+                                                     [Kd::is_fp4 ? 16 : 16 * RBY];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
@@ -268,6 +276,7 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
   int cur_b = -1, cur_j = -1;
   Work w;
   i32x4 qv[4];
+  int qs = 127;                  // MXFP4: the query scale of this lane's 32-element group
   int lim = -1, lim_lo = -1, start = 0;
   // Paged keys: page indices of this wave's next blocks of the tile, lane k
   // holding the k-th (blocks beta, beta + 4, ...), read with readlane; pk is
@@ -301,7 +310,12 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
       if (row_ok) {
         const uint8_t* qr =
             p.q + ((int64_t)(w.t0 + ti) * p.Hq + (hk * p.g + hg)) * kD * Kd::q_bytes;
-        if constexpr (Kd::is_f8) {
+        if constexpr (Kd::is_fp4) {
+          // 32-element group G of the row (B operand) and its scale byte
+          const int64_t qrow = (int64_t)(w.t0 + ti) * p.Hq + (hk * p.g + hg);
+          qv[0] = ld16(p.q + qrow * (kD / 2) + 16 * G);
+          qs = p.q_mx[qrow * (kD / 32) + G];
+        } else if constexpr (Kd::is_f8) {
           qv[0] = ld16(qr + 32 * G);
           qv[1] = ld16(qr + 32 * G + 16);
         } else {
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
     }
 
     const int beta = c.beta;
-    int64_t boff, soff;         // key byte offset, int8 scale element offset
+    int64_t boff, soff;         // key byte offset, int8 scale element (MXFP4: byte) offset
     if (p.paged) {
       if (pk == 64) {
         const int bb = beta + 4 * l;
@@ -327,10 +341,13 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
       const int page = __builtin_amdgcn_readlane(pidx, pk);
       ++pk;
       boff = (int64_t)page * p.k_page_stride;
-      soff = (int64_t)page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
+      soff = Kd::is_fp4 ? (int64_t)page * p.mx_page_stride + (int64_t)hk * p.mx_head_stride
+                        : (int64_t)page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
     } else {
       boff = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
-      soff = (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
+      soff = Kd::is_fp4
+                 ? (w.koff + (int64_t)beta * kP) * p.mx_row_stride + (int64_t)hk * p.mx_head_stride
+                 : (w.koff + (int64_t)beta * kP) * p.s_row_stride + (int64_t)hk * p.s_head_stride;
     }
     // wave-uniform block base (scalar registers); per-lane offsets within a
     // block fit 32 bits (checked on the host), which gives the loads the
@@ -348,7 +365,41 @@ __global__ __launch_bounds__(256, Kind<KK>::is_i8 ? 3 : 2) void decode_kernel(Pa
     }
 
     float m;
-    if constexpr (Kd::is_f8 || Kd::is_i8) {
+    if constexpr (Kd::is_fp4) {
+      // MXFP4: instruction s reads tokens 16s..16s+15 whole (64 bytes each,
+      // one contiguous KB), lane (n, G) taking 32-element group G of token
+      // 16s + n: the A operand of a 16x16x128 scaled MFMA as loaded.  The
+      // scale word of the same token holds the four group scales.  Token rows
+      // past kv_len re-read the last valid row (in bounds; masked).
+      const uint8_t* sb = p.k_mx + uniform64(soff);
+      i32x4 a[8];
+      uint32_t sw[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int row = min(16 * s + n, nvalid - 1);
+        a[s] = ld16_stream(kb + (uint32_t)(row * p.k_row_stride + 16 * G));
+        sw[s] = *reinterpret_cast<const uint32_t*>(sb + (uint32_t)(row * p.mx_row_stride));
+      }
+      auto score = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        float mm = -__builtin_inff();
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f32x4 acc = mfma16x16x128_fp4(a[s], qv[0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                              (sw[s] >> (8 * G)) & 255, qs);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int jr = 16 * s + 4 * G + r;          // key token of acc[r]
+            float v = acc[r];
+            if constexpr (MASKED) v = (beta * kP + jr <= lim) ? v : -__builtin_inff();
+            mm = fmaxf(mm, v);
+          }
+        }
+        return mm;
+      };
+      if (pend_ok) *pend_ptr = pend_val;
+      m = full ? score(std::false_type{}) : score(std::true_type{});
+    } else if constexpr (Kd::is_f8 || Kd::is_i8) {
       // Key loads: instruction i reads rows 8i..8i+7 of the block whole (lane
       // l: row 8i + l/8, 16-byte chunk l%8), eight full 128-byte lines per
       // instruction.  (Loading straight into the MFMA operand layout would
@@ -904,140 +955,6 @@ void prefill_kernel(Params p) {
         *reinterpret_cast<f32x4*>(orow_ptr[u] + beta) = v;
       }
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// MXFP4 on short query runs (decode batches): one wave per work item of
-// `locate` -- a 16-row tile (hpt heads x tpt tokens of one KV group) over a
-// range of kMxDecodeChunk blocks.  Each 16-token sub-tile of a key block is
-// one MFMA 16x16x128 (the whole 128-deep row): key tokens on the M side,
-// query rows on the N side.  Lane l loads 16 bytes of token l % 16 (group
-// l / 16), so the 64 lanes of one load read 16 whole 64-byte token rows, and
-// the token's scale word; the next block's loads are issued before the
-// current block's product.  HBM-bound: every visible key byte is read once.
-// ---------------------------------------------------------------------------
-constexpr int kMxDecodeChunk = 8;
-
-__global__ __launch_bounds__(64) void decode_mx_kernel(Params p) {
-  const Work w = locate(p);
-  if (!w.valid) return;
-  const int l = lane_id();
-  const int n = l & 15;          // key token of a sub-tile (A) / query row (B and results)
-  const int G = l >> 4;          // 32-element group of the row
-  const int i0 = w.t0 - p.cu_q[w.b];
-  const int ti = n / p.hpt;
-  const int hg = w.hc * p.hpt + (n - ti * p.hpt);
-  const bool row_ok = n < p.hpt * p.tpt && ti < w.ntok && hg < p.g;
-  const int lim = (row_ok && w.L > 0) ? last_visible(p, w, i0 + ti) : -1;
-  const bool tile_ok = w.L > 0 && w.ntok > 0;
-  const int lim_lo = __builtin_amdgcn_readfirstlane(tile_ok ? last_visible(p, w, i0) : -1);
-  const int lim_hi = tile_ok ? last_visible(p, w, i0 + w.ntok - 1) : -1;
-  const int nb = min((w.L + kP - 1) / kP, p.MB);
-  // the block loop's bounds are the same on every lane; readfirstlane puts
-  // them in scalar registers, so that the loop is not compiled as a divergent
-  // one (whose merged wait counts would stall on the loads in flight)
-  const int vend = __builtin_amdgcn_readfirstlane(
-      max(w.c0, min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0)));
-  const int c0 = __builtin_amdgcn_readfirstlane(w.c0);
-  const int anchor = local_anchor(p, w, i0 + ti);
-  float* const orow =
-      p.out + (((int64_t)w.hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W;
-
-  // query row n, group G (B operand) and its scale byte
-  i32x4 qv = i32x4{0, 0, 0, 0};
-  int qs = 127;
-  if (row_ok && c0 < vend) {
-    const int64_t qrow = (int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg);
-    qv = ld16(p.q + qrow * (kD / 2) + 16 * G);
-    qs = p.q_mx[qrow * (kD / 32) + G];
-  }
-
-  // page indices of the work item's blocks, one per lane, read with readlane
-  // (a table read inside the loop would wait for the key loads in flight)
-  int pidx = 0;
-  if (p.paged && l < vend - c0) pidx = p.block_table[(int64_t)w.b * p.MB + c0 + l];
-
-  // a block's eight A fragments (16 bytes of token 16 s + n) and those
-  // tokens' scale words; rows past kv_len read row 0 (masked later)
-  auto load = [&](int beta, i32x4 (&a)[8], uint32_t (&sc)[8]) {
-    int64_t kb, sb;
-    if (p.paged) {
-      const int64_t page = __builtin_amdgcn_readlane(pidx, beta - c0);
-      kb = page * p.k_page_stride;
-      sb = page * p.mx_page_stride;
-    } else {
-      kb = (w.koff + (int64_t)beta * kP) * p.k_row_stride;
-      sb = (w.koff + (int64_t)beta * kP) * p.mx_row_stride;
-    }
-    const uint8_t* kp = p.k + uniform64(kb + (int64_t)w.hk * p.k_head_stride);
-    const uint8_t* sp = p.k_mx + uniform64(sb + (int64_t)w.hk * p.mx_head_stride);
-    const int nvalid = min(kP, w.L - beta * kP);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int jj = 16 * s + n;
-      const int src = jj < nvalid ? jj : 0;
-      a[s] = ld16_stream(kp + (uint32_t)(src * p.k_row_stride + 16 * G));
-      sc[s] = *reinterpret_cast<const uint32_t*>(sp + (uint32_t)(src * p.mx_row_stride));
-    }
-  };
-
-  bool pend_ok = false;
-  float* pend_ptr = orow;
-  float pend_val = 0.f;
-  // one block's scores from its fragments, after the previous block's
-  // result is stored (the caller has issued the next block's loads first)
-  auto step = [&](int beta, const i32x4 (&ka)[8], const uint32_t (&sa)[8]) {
-    if (pend_ok) *pend_ptr = pend_val;
-    const bool full = beta * kP + kP - 1 <= lim_lo;
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f32x4 acc =
-          mfma16x16x128_fp4(ka[s], qv, f32x4{0.f, 0.f, 0.f, 0.f}, (sa[s] >> (8 * G)) & 255, qs);
-      // acc[k] is key token 16 s + 4 G + k of row n
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float v = acc[k];
-        if (!full) v = (beta * kP + 16 * s + 4 * G + k <= lim) ? v : -__builtin_inff();
-        m = fmaxf(m, v);
-      }
-    }
-    // the four groups hold disjoint tokens of the same row
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    pend_ok = G == 0 && row_ok;
-    pend_ptr = orow + beta;
-    pend_val = finish(p, w.L, anchor, beta, true, m);
-  };
-  // two register buffers used in turn, one block ahead (a copy between them
-  // would wait for the loads in flight); the loop has no exit between its
-  // two halves, which would make the compiler wait there as well
-  i32x4 fa[8], fb[8];
-  uint32_t ca[8], cb[8];
-  if (c0 < vend) {
-    load(c0, fa, ca);
-    int beta = c0;
-    for (; beta + 2 < vend; beta += 2) {
-      load(beta + 1, fb, cb);
-      step(beta, fa, ca);
-      load(beta + 2, fa, ca);
-      step(beta + 1, fb, cb);
-    }
-    if (beta + 1 < vend) {
-      load(beta + 1, fb, cb);
-      step(beta, fa, ca);
-      step(beta + 1, fb, cb);
-    } else {
-      step(beta, fa, ca);
-    }
-  }
-  if (pend_ok) *pend_ptr = pend_val;
-  // the work item's columns past the visible blocks: -inf and local_mask,
-  // four columns per row pass (lane group G takes columns G, G + 4, ...)
-  if (row_ok) {
-    for (int beta = vend + G; beta < w.c1; beta += 4)
-      orow[beta] = finish(p, w.L, anchor, beta, false, 0.f);
   }
 }
 

@@ -196,10 +196,11 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
  *              4-byte aligned, like query_scale.
  * local_mode   msa_local_mode_t.  Everything else as msa_index_score.
  *
- * It always runs on the prefill tiles.  Returns as msa_index_score, plus
- * MSA_ERR_DTYPE unless query and key are MSA_DTYPE_MXFP4 and MSA_ERR_NULL
- * for a NULL scale.  (msa_index_score and its variants return MSA_ERR_SCALE
- * for MXFP4 tensors: they cannot carry the group scales.) */
+ * The kernel family is picked from the sizes, as msa_index_score does.
+ * Returns as msa_index_score, plus MSA_ERR_DTYPE unless query and key are
+ * MSA_DTYPE_MXFP4 and MSA_ERR_NULL for a NULL scale.  (msa_index_score and
+ * its variants return MSA_ERR_SCALE for MXFP4 tensors: they cannot carry the
+ * group scales.) */
 msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* query_scale,
                                    const msa_tensor_t* key, const uint8_t* key_scale,
                                    const int32_t* start_loc, const int32_t* block_table,
@@ -208,6 +209,19 @@ msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* que
                                    int32_t sparse_mode, int32_t init_blocks,
                                    int32_t local_blocks, int32_t local_mode, float* out,
                                    int64_t out_width, void* stream);
+
+/* Same as msa_index_score_mxfp4, with the kernel family chosen by the caller
+ * as for msa_index_score_family (-1 from the sizes, 0 the decode tiles, 1 the
+ * prefill tiles; any other value returns MSA_ERR_ATTR).  For tests and
+ * benchmarks. */
+msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8_t* query_scale,
+                                          const msa_tensor_t* key, const uint8_t* key_scale,
+                                          const int32_t* start_loc, const int32_t* block_table,
+                                          int64_t max_blocks, const int32_t* cu_seqlens_q,
+                                          const int32_t* kv_len, int32_t batch, int32_t layout,
+                                          int32_t sparse_mode, int32_t init_blocks,
+                                          int32_t local_blocks, int32_t local_mode, float* out,
+                                          int64_t out_width, void* stream, int32_t family);
 
 /* Top-k block selection on the score rows: the stage the pages place after
  * the block score (the notes "MiniMax Sparse Attention: paper algorithm and

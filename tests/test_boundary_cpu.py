@@ -225,13 +225,16 @@ def test_local_mode_rules():
 
 
 def mx_call(q=None, k=None, *, qs=FAKE, ks=FAKE, start=FAKE, table=FAKE, mb=2, cu=FAKE,
-            kv=FAKE, B=1, layout=1, mode=3, init=0, local=1, local_mode=0, out=FAKE, width=16):
+            kv=FAKE, B=1, layout=1, mode=3, init=0, local=1, local_mode=0, out=FAKE, width=16,
+            family=None):
     lib = m.load_library()
     q = q if q is not None else tdesc([32, 8, 64], dtype=5)
     k = k if k is not None else tdesc([8, 128, 1, 64], dtype=5)
-    return lib.msa_index_score_mxfp4(ctypes.byref(q), qs, ctypes.byref(k), ks, start, table, mb,
-                                     cu, kv, B, layout, mode, init, local, local_mode, out,
-                                     width, None)
+    args = (ctypes.byref(q), qs, ctypes.byref(k), ks, start, table, mb, cu, kv, B, layout, mode,
+            init, local, local_mode, out, width, None)
+    if family is None:
+        return lib.msa_index_score_mxfp4(*args)
+    return lib.msa_index_score_mxfp4_family(*args, family)
 
 
 def test_mxfp4_rules():
@@ -248,6 +251,14 @@ def test_mxfp4_rules():
     assert mx_call(ks=FAKE + 1) == STRIDE
     assert mx_call(local_mode=3) == ATTR
     assert mx_call(mode=1) == ATTR
+    # the family entry: -1, 0, 1 accepted, anything else rejected; the same
+    # checks otherwise
+    for fam in (-1, 0, 1):
+        assert mx_call(q=q0, family=fam) == OK
+        assert mx_call(qs=None, family=fam) == NULL
+    assert mx_call(q=q0, family=2) == ATTR
+    assert mx_call(q=q0, family=-2) == ATTR
+    assert mx_call(q=tdesc([4, 8, 128], dtype=0), family=0) == DTYPE
     # the other entries cannot carry the group scales
     assert call(q=tdesc([4, 8, 64], dtype=5), k=tdesc([8, 128, 1, 64], dtype=5)) == SCALE
     assert call(q=tdesc([4, 8, 64], dtype=5), k=tdesc([8, 128, 1, 64], dtype=5),

@@ -53,7 +53,7 @@ def to_device(case, dev):
 
 def run_gpu(case, dev, family=-1):
     """The GPU output of a case through the C ABI (MXFP4 cases take their own
-    entry, which always runs the prefill tiles, whatever ``family`` says)."""
+    entry)."""
     import block_max_qk_amd as m
     d = to_device(case, dev)
     W = m.msa_index_score_out_width(case.max_blocks)
@@ -62,7 +62,7 @@ def run_gpu(case, dev, family=-1):
         m.msa_index_score_mxfp4(d["query"], d["q_mx"], d["key"], d["k_mx"], d["start_loc"],
                                 d["block_table"], d["cu_seqlens_q"], d["kv_len"], case.layout,
                                 case.sparse_mode, case.init_blocks, case.local_blocks, out,
-                                case.max_blocks, local_mode=case.local_mode)
+                                case.max_blocks, local_mode=case.local_mode, family=family)
         torch.cuda.synchronize()
         return out.cpu()
     m.msa_index_score(d["query"], d["key"], d["start_loc"], d["block_table"], d["scale"],
