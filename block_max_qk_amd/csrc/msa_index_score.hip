@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 
 #include "msa_kernels.hpp"
@@ -66,14 +67,25 @@ hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
     return hipGetLastError();
   }
   // Decode: one round of workgroups, as many as fit on the device at once,
-  // split evenly over the units (KV head x head chunk).
-  int dev = 0, cus = 0, per_cu = 0;
+  // split evenly over the units (KV head x head chunk).  The device's slot
+  // count for this kernel is looked up once per device (the runtime queries
+  // cost microseconds, as much as a short decode launch).
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int64_t> slots_of[kMaxDevices];
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK>, 256, 0);
   if (e != hipSuccess) return e;
-  const int64_t slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  int64_t slots = cached ? slots_of[dev].load(std::memory_order_relaxed) : 0;
+  if (slots == 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK>, 256, 0);
+    if (e != hipSuccess) return e;
+    slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+    if (cached) slots_of[dev].store(slots, std::memory_order_relaxed);
+  }
   const int64_t gu = std::max<int64_t>(1, slots / p.units);
   hipLaunchKernelGGL(msa::decode_kernel<KK>, dim3((unsigned)(gu * p.units)), dim3(256), 0, s, p);
   return hipGetLastError();
