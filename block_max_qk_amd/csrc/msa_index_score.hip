@@ -97,7 +97,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
                  const int32_t* cu_seqlens_q, const int32_t* kv_len, int32_t batch,
                  int32_t layout, int32_t sparse_mode, int32_t init_blocks,
                  int32_t local_blocks, int32_t local_mode, float* out, int64_t out_width,
-                 void* stream, int32_t family) {
+                 void* stream, int32_t family, bool mx_entry) {
   // Pointers that a call with no requests (B = 0) or no query tokens (T = 0)
   // never reads may be NULL there; torch hands empty tensors a NULL address.
   // start_loc is not read with the per-query local window.
@@ -114,16 +114,18 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (!pair_ok(query->dtype, key->dtype)) return MSA_ERR_DTYPE;
   const bool is_i8 = key->dtype == MSA_DTYPE_I8;
   if (is_i8 != (scale != nullptr)) return MSA_ERR_SCALE;
-  // MXFP4 takes its E8M0 group scales (and nothing else does); its last axis
+  // MXFP4 comes through its own entry only, the one that carries the E8M0
+  // group scales (and only it takes scales of that kind); its last axis
   // holds D/2 bytes
   const bool is_mx = key->dtype == MSA_DTYPE_MXFP4;
-  if (is_mx != (q_mx != nullptr) || is_mx != (k_mx != nullptr)) return MSA_ERR_SCALE;
+  if (is_mx != mx_entry || (!is_mx && (q_mx || k_mx))) return MSA_ERR_SCALE;
   const int64_t DB = is_mx ? msa::kD / 2 : msa::kD;     // stored last-axis extent
 
   // query [T, Hq, D], compact
   if (query->ndim != 3) return MSA_ERR_SHAPE;
   const int64_t T = query->shape[0], Hq = query->shape[1], D = query->shape[2];
   if (T < 0 || Hq < 1 || D != DB) return MSA_ERR_SHAPE;
+  if (is_mx && T > 0 && (!q_mx || !k_mx)) return MSA_ERR_NULL;
   if (!compact_axis(D, query->stride[2], 1) || !compact_axis(Hq, query->stride[1], D) ||
       !compact_axis(T, query->stride[0], Hq * D))
     return MSA_ERR_STRIDE;
@@ -305,7 +307,7 @@ msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
                              int64_t out_width, void* stream) {
   return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
              cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             MSA_LOCAL_PER_REQUEST, out, out_width, stream, -1);
+             MSA_LOCAL_PER_REQUEST, out, out_width, stream, -1, false);
 }
 
 msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_t* key,
@@ -317,7 +319,7 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     int64_t out_width, void* stream, int32_t family) {
   return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
              cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             MSA_LOCAL_PER_REQUEST, out, out_width, stream, family);
+             MSA_LOCAL_PER_REQUEST, out, out_width, stream, family, false);
 }
 
 msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* key,
@@ -329,7 +331,7 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
                                 float* out, int64_t out_width, void* stream, int32_t family) {
   return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
              cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             local_mode, out, out_width, stream, family);
+             local_mode, out, out_width, stream, family, false);
 }
 
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
@@ -389,10 +391,9 @@ msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* que
                                    int64_t out_width, void* stream) {
   if (!query || !key) return MSA_ERR_NULL;
   if (query->dtype != MSA_DTYPE_MXFP4 || key->dtype != MSA_DTYPE_MXFP4) return MSA_ERR_DTYPE;
-  if (!query_scale || !key_scale) return MSA_ERR_NULL;
   return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
              cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             local_mode, out, out_width, stream, -1);
+             local_mode, out, out_width, stream, -1, true);
 }
 
 msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8_t* query_scale,
@@ -405,10 +406,9 @@ msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8
                                           int64_t out_width, void* stream, int32_t family) {
   if (!query || !key) return MSA_ERR_NULL;
   if (query->dtype != MSA_DTYPE_MXFP4 || key->dtype != MSA_DTYPE_MXFP4) return MSA_ERR_DTYPE;
-  if (!query_scale || !key_scale) return MSA_ERR_NULL;
   return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
              cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             local_mode, out, out_width, stream, family);
+             local_mode, out, out_width, stream, family, true);
 }
 
 int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }

@@ -198,7 +198,8 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
  *
  * The kernel family is picked from the sizes, as msa_index_score does.
  * Returns as msa_index_score, plus MSA_ERR_DTYPE unless query and key are
- * MSA_DTYPE_MXFP4 and MSA_ERR_NULL for a NULL scale.  (msa_index_score and
+ * MSA_DTYPE_MXFP4 and MSA_ERR_NULL for a NULL scale when T > 0 (with no
+ * query tokens nothing is read and both scales may be NULL).  (msa_index_score and
  * its variants return MSA_ERR_SCALE for MXFP4 tensors: they cannot carry the
  * group scales.) */
 msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* query_scale,

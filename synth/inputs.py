@@ -607,6 +607,38 @@ def random_cases(n: int, seed: int = 4242) -> List[MsaCase]:
     return out
 
 
+def mx_random_cases(n: int, seed: int = 9090) -> List[MsaCase]:
+    """n small MXFP4 cases with the knobs drawn at random as in random_cases
+    (lengths, heads, layout, mode, local_mask counts and window, table width,
+    dim0 gap); query and key are both MXFP4."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 6))
+        q_lens = [int(x) for x in rng.choice([0, 1, 2, 3, 5, 17, 40, 90], size=B)]
+        kv_lens = [int(x) for x in rng.choice([0, 1, 100, 127, 128, 129, 300, 511, 700],
+                                               size=B)]
+        Hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 3, 8, 16, 20]))
+        layout = str(rng.choice(["BBND", "BNBD", "TND"]))
+        mode = int(rng.choice([0, 3]))
+        nb = max(1, max(-(-k // 128) for k in kv_lens))
+        MB = None if layout == "TND" else nb + int(rng.integers(0, 20))
+        limit = (MB if MB is not None else ((nb + 15) // 16) * 16)
+        init = int(rng.integers(0, min(3, limit) + 1))
+        local = int(rng.integers(0, min(3, limit) + 1))
+        starts = [int(rng.integers(0, MB if MB is not None else nb)) for _ in range(B)]
+        gap = int(rng.choice([0, 0, 1])) if layout != "TND" else 0
+        local_mode = int(rng.integers(0, 2))
+        out.append(make_case(f"mxrand{i}_{layout.lower()}_g{g}", seed + 1 + i,
+                             q_lens=q_lens, kv_lens=kv_lens, Hq=Hkv * g, Hkv=Hkv,
+                             qdtype="mxfp4", layout=layout, MB=MB,
+                             extra_pages=int(rng.integers(0, 4)), gap=gap, sparse_mode=mode,
+                             init_blocks=init, local_blocks=local, start_loc=starts,
+                             local_mode=local_mode))
+    return out
+
+
 def case_summary(case: MsaCase) -> dict:
     return {
         "name": case.name, "layout": case.layout, "q": case.query_dtype_name(),

@@ -243,6 +243,7 @@ def test_mxfp4_rules():
     assert mx_call(q=q0, k=tdesc([300, 1, 64], dtype=5), layout=0, table=None, mb=3) == OK
     assert mx_call(qs=None) == NULL                                   # scales are required
     assert mx_call(ks=None) == NULL
+    assert mx_call(q=q0, qs=None, ks=None) == OK                      # ... unless T = 0
     assert mx_call(q=tdesc([4, 8, 128], dtype=0)) == DTYPE            # not MXFP4
     assert mx_call(k=tdesc([8, 128, 1, 128], dtype=1)) == DTYPE
     assert mx_call(q=tdesc([4, 8, 128], dtype=5)) == SHAPE            # 64 bytes per row

@@ -130,6 +130,15 @@ def test_brute_force_agreement_random(idx):
     assert_close_ulp(oracle.index_score_case(c), brute_force(c))
 
 
+MX_RANDOM = synth.mx_random_cases(12)
+
+
+@pytest.mark.parametrize("idx", range(len(MX_RANDOM)), ids=[c.name for c in MX_RANDOM])
+def test_brute_force_agreement_mx_random(idx):
+    c = MX_RANDOM[idx]
+    assert_close_ulp(oracle.index_score_case(c), brute_force(c))
+
+
 # ---------------------------------------------------------------------------
 # closed forms of the causal window
 # ---------------------------------------------------------------------------

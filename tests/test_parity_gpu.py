@@ -107,6 +107,18 @@ def test_random_sweep_parity(idx, family, dev):
     assert r["ok"], r
 
 
+MX_RANDOM = synth.mx_random_cases(12)
+
+
+@pytest.mark.parametrize("family", [0, 1])
+@pytest.mark.parametrize("idx", range(len(MX_RANDOM)), ids=[c.name for c in MX_RANDOM])
+def test_mx_random_sweep_parity(idx, family, dev):
+    c = MX_RANDOM[idx]
+    log(f"[gpu] mx random {c.name} family={family} {synth.case_summary(c)}")
+    r = check(oracle_out(c), run_gpu(c, dev, family), tol_of(c))
+    assert r["ok"], r
+
+
 @pytest.mark.parametrize("family", [0, 1])
 @pytest.mark.parametrize("idx", range(len(PAGED)), ids=[c.name for c in PAGED])
 def test_poison_invariance(idx, family, dev):
