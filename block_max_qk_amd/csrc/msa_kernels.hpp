@@ -39,6 +39,7 @@ constexpr int kPrefillRows = 256;   // family choice threshold: half of this per
 // varlen prefill 4.00 ms with 16, 3.90 ms with 32, 3.99 ms with 64; fp8 and
 // MXFP4 within 2% between 32 and 64).
 constexpr int kPrefillChunk = 32;
+constexpr int kPrefillWaves = 4;   // waves per prefill workgroup
 
 // 32-row MFMA N tiles each prefill wave holds; a workgroup's tile is four
 // waves of them.  More N tiles let one key fragment read from LDS feed more
@@ -548,20 +549,31 @@ void prefill_kernel(Params p) {
   // Key blocks pass through an LDS ring of stages.  16-bit keys: stages of 64
   // tokens (16 KB), three deep, so a stage's copy has two compute periods to
   // land; fp8: whole 128-token blocks (16 KB), two deep; MXFP4: whole blocks
-  // (8 KB of values plus 512 B of scales), two deep; int8 (widened to fp16
-  // through registers): whole blocks (32 KB), two deep.  All of it fits three
-  // workgroups per CU (two for int8).
+  // (8 KB; their scales are staged for the whole work item up front), three
+  // deep; int8 (widened to fp16 through registers): whole blocks (32 KB), two
+  // deep.  All of it fits three workgroups per CU (two for int8).
   constexpr int RB = Kd::is_fp4 ? 64 : (Kd::is_f8 ? 128 : 256);   // LDS bytes per key token
   constexpr bool ASYNC = !Kd::is_i8;           // copy HBM/L2 -> LDS directly
   constexpr int ST = (ASYNC && RB == 256) ? 64 : kP;   // tokens per stage
   constexpr int SPB = kP / ST;                 // stages per block
-  constexpr int RING = SPB == 2 ? 3 : 2;
+  constexpr int RING = (SPB == 2 || Kd::is_fp4) ? 3 : 2;
   constexpr int SBYTES = ST * RB;
   constexpr int NI = SBYTES / 1024 / 4;        // copy instructions per wave per stage
-  static_assert(!ASYNC || RING == 2 || NI == 4,
-                "the three-deep ring's wait counts assume four copies per wave per stage");
+  static_assert(!ASYNC || RING == 2 || NI == (Kd::is_fp4 ? 2 : 4),
+                "the three-deep ring's wait counts assume these copies per wave per stage");
   __shared__ __attribute__((aligned(16))) uint8_t kl[RING * SBYTES];
   __shared__ float scl[2][kP];
+  // MXFP4: the scale words of every block of the work item, lane-major:
+  // [block][n][mt] holds token 32 mt + n's word, so that lane (n, G) reads its
+  // block's four M tiles with one 16-byte LDS read.  Staged once, before the
+  // block loop, so that the loop issues no register loads: with register
+  // loads in flight beside the LDS copies (and stores) the compiler waits for
+  // every memory operation before using them.
+  __shared__ __attribute__((aligned(16))) uint32_t kmx[Kd::is_fp4 ? kPrefillChunk : 1][32][4];
+  // MXFP4: each wave's copy of the work item's page indices, read per lane
+  // while staging the scales (readlane of the index register made the
+  // compiler wait for every load in flight before each one)
+  __shared__ int32_t kpg[Kd::is_fp4 ? kPrefillWaves : 1][kPrefillChunk];
 
   const Work w = locate(p);
   if (!w.valid) return;
@@ -665,31 +677,39 @@ void prefill_kernel(Params p) {
         reinterpret_cast<const void*>(kb + (uint32_t)(src * p.k_row_stride + 16 * c)),
         (__attribute__((address_space(3))) void*)(kl + slot * SBYTES + X * 1024), 16, 0, 0);
   };
-  // MXFP4: the scale words of this lane's key token in each of the block's
-  // four M tiles (token 32 mt + n), loaded into registers one stage ahead,
-  // with that stage's copies (rows past kv_len read row 0).  (Staged in LDS
-  // instead, the copies made every later LDS read of the stage wait for
-  // them.)
-  uint32_t ksw_next[Kd::is_fp4 ? 4 : 1];
-  auto load_scales = [&](int sg) {
-    const int beta = w.c0 + sg / SPB;
-    const int64_t base =
-        (p.paged ? (int64_t)__builtin_amdgcn_readlane(pidx, beta - w.c0) * p.mx_page_stride
-                 : (w.koff + (int64_t)beta * kP) * p.mx_row_stride) +
-        (int64_t)w.hk * p.mx_head_stride;
-    const uint8_t* sb = p.k_mx + uniform64(base);
-    const int nvalid = min(kP, w.L - beta * kP);
+  // MXFP4: stage the scale words of the work item's nblk blocks into kmx
+  // (rows past kv_len read row 0; their scores are masked).  Entry e = tid +
+  // 256 i is token e % 128 of block e / 128 (the same block across a wave);
+  // all loads are issued before the first LDS write (entries past the last
+  // block re-read it and are not written).
+  auto stage_scales = [&](int nblk) {
+    constexpr int NE = kPrefillChunk * kP / 256;
+    if (p.paged && l < kPrefillChunk) kpg[wave][l] = pidx;
+    wave_lds_sync();
+    uint32_t sv4[NE];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int jj = mt * 32 + n;
+    for (int i = 0; i < NE; ++i) {
+      const int e = tid + 256 * i;
+      const int bi = min(e / kP, nblk - 1);
+      const int jj = e % kP;
+      const int beta = w.c0 + bi;
+      const int64_t base =
+          (p.paged ? (int64_t)kpg[wave][bi] * p.mx_page_stride
+                   : (w.koff + (int64_t)beta * kP) * p.mx_row_stride) +
+          (int64_t)w.hk * p.mx_head_stride;
+      const int nvalid = min(kP, w.L - beta * kP);
       const int src = jj < nvalid ? jj : 0;
-      ksw_next[mt] = *reinterpret_cast<const uint32_t*>(sb + (uint32_t)(src * p.mx_row_stride));
+      sv4[i] = *reinterpret_cast<const uint32_t*>(p.k_mx + base + (int64_t)src * p.mx_row_stride);
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = tid + 256 * i;
+      if (e < nblk * kP) kmx[e / kP][e & 31][(e % kP) >> 5] = sv4[i];
     }
   };
   auto stage_async = [&](int sg, int slot, int64_t kbytes) {
 #pragma unroll
     for (int q = 0; q < NI; ++q) stage_copy(q, sg, slot, kbytes);
-    if constexpr (Kd::is_fp4) load_scales(sg);
   };
   auto gload_i8 = [&](int beta) {
     const uint8_t* kb = p.k + block_bytes(beta) + (int64_t)w.hk * p.k_head_stride;
@@ -742,6 +762,10 @@ void prefill_kernel(Params p) {
 #pragma unroll
     for (int sg = 0; sg < RING - 1; ++sg)
       if (sg < nst) stage_async(sg, sg, sg < SPB ? kb0 : block_bytes(w.c0 + sg / SPB));
+    // (the loop's first barrier makes every wave's writes visible)
+    if constexpr (Kd::is_fp4) {
+      if (nst > 0) stage_scales(vend - w.c0);
+    }
   } else {
     if (nst > 0) {
       gload_i8(w.c0);
@@ -788,10 +812,15 @@ void prefill_kernel(Params p) {
     // Stage sg has landed (the one copy still allowed in flight is the next
     // stage's) and every wave is done with the slot the copy below reuses.
     // Written out because a plain __syncthreads() would wait for all copies.
-    if (RING == 3 && sg + 1 < nst)
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
+    // (the next stage's NI copies may stay in flight)
+    if (RING == 3 && sg + 1 < nst) {
+      if constexpr (NI == 4)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     // a finished group of results is written here, ahead of the next
     // copies, so that the copies stay the newest memory operations the
     // waits count
@@ -848,11 +877,14 @@ void prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
       f32x16 acc[NTW];
-      // MXFP4: this block's scale words (loaded during the previous stage)
+      // MXFP4: this block's scale words, token 32 mt + n in word mt
       uint32_t ksw[Kd::is_fp4 ? 4 : 1];
       if constexpr (Kd::is_fp4) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ksw[mt] = ksw_next[mt];
+        const uint4 kw = *reinterpret_cast<const uint4*>(&kmx[beta - w.c0][n][0]);
+        ksw[0] = kw.x;
+        ksw[1] = kw.y;
+        ksw[2] = kw.z;
+        ksw[3] = kw.w;
       }
 #pragma unroll
       for (int i = 0; i < NFR; ++i) {
@@ -865,9 +897,6 @@ void prefill_kernel(Params p) {
 #pragma unroll
             for (int q = 0; q < NI / CPTS; ++q)
               stage_copy((i / (NFR / CPTS)) * (NI / CPTS) + q, csg, csg % RING, ckb);
-            if constexpr (Kd::is_fp4) {
-              if (i == 0) load_scales(csg);
-            }
           }
         }
         if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
