@@ -856,7 +856,8 @@ void prefill_kernel(Params p) {
       // LEAD + 1 fragments live.
       constexpr int PER_MT = Kd::is_fp4 ? 2 : Kd::is_f8 ? 4 : 8;   // fragments per M tile
       constexpr int NFR = (ST / 32) * PER_MT;
-      constexpr int LEAD = Kd::is_fp4 ? 2 : Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
+      // (MXFP4: 4 measured 1% faster than 2, and the same as 6 or 8)
+      constexpr int LEAD = (Kd::is_fp4 || Kd::is_f8) ? 4 : (NTW >= 3 ? 1 : 2);
       auto frag = [&](int i) -> i32x4 {
         const int mt = i / PER_MT, q = i % PER_MT;
         const int jj = mt * 32 + n;
