@@ -272,7 +272,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hchunks = (g + p.hpt - 1) / p.hpt;
   // prefill units: (KV head, head chunk, block chunk); decode units: (KV
   // head, head chunk), each walking its own copy of the batch's work list
-  p.chunk = msa::kPrefillChunk;
+  p.chunk = msa::prefill_chunk(is_mx ? msa::KMXFP4 : key->dtype);
   p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
   p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;

@@ -35,10 +35,16 @@ namespace msa {
 constexpr int kDecodeRows = 16;
 constexpr int kPrefillRows = 256;   // family choice threshold: half of this per request
 // Blocks per prefill work item: the work item's query tile and ring set-up
-// are amortised over them.  32 measured fastest for every key type (bf16
-// varlen prefill 4.00 ms with 16, 3.90 ms with 32, 3.99 ms with 64; fp8 and
-// MXFP4 within 2% between 32 and 64).
+// are amortised over them.  32 measured fastest for the 16-bit and 8-bit key
+// types (bf16 varlen prefill 4.00 ms with 16, 3.90 ms with 32, 3.99 ms with
+// 64; fp8 within 2% between 32 and 64).
 constexpr int kPrefillChunk = 32;
+// MXFP4 blocks cost a quarter of the MFMA time of 16-bit ones, so its work
+// items are longer, to spread their fixed costs (the scale staging among them):
+// varlen prefill 1.345 ms with 32, 1.313 with 48, 1.338 with 64; chunked
+// prefill 2.23, 2.19, 2.17-2.19 ms
+constexpr int kMxPrefillChunk = 48;
+constexpr int prefill_chunk(int kk) { return kk == KMXFP4 ? kMxPrefillChunk : kPrefillChunk; }
 constexpr int kPrefillWaves = 4;   // waves per prefill workgroup
 
 // 32-row MFMA N tiles each prefill wave holds; a workgroup's tile is four
@@ -569,11 +575,13 @@ void prefill_kernel(Params p) {
   // block loop, so that the loop issues no register loads: with register
   // loads in flight beside the LDS copies (and stores) the compiler waits for
   // every memory operation before using them.
-  __shared__ __attribute__((aligned(16))) uint32_t kmx[Kd::is_fp4 ? kPrefillChunk : 1][32][4];
+  constexpr int CHUNK = prefill_chunk(KK);     // blocks per work item at most
+  static_assert(CHUNK <= 64, "page indices are held one per lane");
+  __shared__ __attribute__((aligned(16))) uint32_t kmx[Kd::is_fp4 ? CHUNK : 1][32][4];
   // MXFP4: each wave's copy of the work item's page indices, read per lane
   // while staging the scales (readlane of the index register made the
   // compiler wait for every load in flight before each one)
-  __shared__ int32_t kpg[Kd::is_fp4 ? kPrefillWaves : 1][kPrefillChunk];
+  __shared__ int32_t kpg[Kd::is_fp4 ? kPrefillWaves : 1][CHUNK];
 
   const Work w = locate(p);
   if (!w.valid) return;
@@ -683,8 +691,8 @@ void prefill_kernel(Params p) {
   // all loads are issued before the first LDS write (entries past the last
   // block re-read it and are not written).
   auto stage_scales = [&](int nblk) {
-    constexpr int NE = kPrefillChunk * kP / 256;
-    if (p.paged && l < kPrefillChunk) kpg[wave][l] = pidx;
+    constexpr int NE = CHUNK * kP / 256;
+    if (p.paged && l < CHUNK) kpg[wave][l] = pidx;
     wave_lds_sync();
     uint32_t sv4[NE];
 #pragma unroll
