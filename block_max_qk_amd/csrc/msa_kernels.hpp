@@ -35,16 +35,17 @@ namespace msa {
 constexpr int kDecodeRows = 16;
 constexpr int kPrefillRows = 256;   // family choice threshold: half of this per request
 // Blocks per prefill work item: the work item's query tile and ring set-up
-// are amortised over them.  32 measured fastest for the 16-bit and 8-bit key
-// types (bf16 varlen prefill 4.00 ms with 16, 3.90 ms with 32, 3.99 ms with
-// 64; fp8 within 2% between 32 and 64).
+// (and for MXFP4 its scale staging) are amortised over them; one A/B each:
+//  16-bit keys: varlen prefill 4.00 ms with 16, 3.90 with 32, 3.99 with 64;
+//               then 4.00 with 32, 3.92 with 40, 3.93 with 48 on another box
+//  fp8:         chunked prefill 3.15 ms with 32, 3.13 with 48 or 64
+//  MXFP4:       varlen prefill 1.345 ms with 32, 1.313 with 48, 1.338 with 64
+//  int8:        32 (no prefill workload of its own)
 constexpr int kPrefillChunk = 32;
-// MXFP4 blocks cost a quarter of the MFMA time of 16-bit ones, so its work
-// items are longer, to spread their fixed costs (the scale staging among them):
-// varlen prefill 1.345 ms with 32, 1.313 with 48, 1.338 with 64; chunked
-// prefill 2.23, 2.19, 2.17-2.19 ms
-constexpr int kMxPrefillChunk = 48;
-constexpr int prefill_chunk(int kk) { return kk == KMXFP4 ? kMxPrefillChunk : kPrefillChunk; }
+constexpr int prefill_chunk(int kk) {
+  return kk == KMXFP4 ? 48 : (kk == KF8E4M3 || kk == KF8E5M2) ? 48
+       : (kk == KF16 || kk == KBF16) ? 40 : kPrefillChunk;
+}
 constexpr int kPrefillWaves = 4;   // waves per prefill workgroup
 
 // 32-row MFMA N tiles each prefill wave holds; a workgroup's tile is four
