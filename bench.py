@@ -361,7 +361,9 @@ def main():
                     help="workload name or index, 'all' (the five base workloads) or 'mx' "
                          "(their MXFP4 variants)")
     ap.add_argument("--copies", type=int, default=0,
-                    help="key-cache copies to rotate over (0: enough to exceed 1 GiB)")
+                    help="key-cache copies to rotate over (0: 4 for the decode workloads, "
+                         "so that the 256 MB Infinity Cache cannot serve a step from the "
+                         "one before; 1 otherwise)")
     ap.add_argument("--family", type=int, default=-1, help="-1 auto, 0 decode, 1 prefill tiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24)
