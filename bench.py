@@ -150,7 +150,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                           ctypes.c_void_p(kmx[i].data_ptr()), ctypes.c_void_p(sl.data_ptr()),
                           None if bt is None else ctypes.c_void_p(bt.data_ptr()),
                           case.max_blocks, ctypes.c_void_p(cu.data_ptr()),
-                          ctypes.c_void_p(kv.data_ptr()), case.batch,
+                          ctypes.c_void_p(kv.data_ptr()), case.batch, case.block_size,
                           m._binding.LAYOUT_CODE[case.layout], case.sparse_mode,
                           case.init_blocks, case.local_blocks, case.local_mode,
                           ctypes.c_void_p(out.data_ptr()), W,
@@ -160,7 +160,8 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
              None if bt is None else ctypes.c_void_p(bt.data_ptr()), case.max_blocks,
              None if scales[i] is None else ctypes.c_void_p(scales[i].data_ptr()),
              ctypes.c_void_p(cu.data_ptr()), ctypes.c_void_p(kv.data_ptr()), case.batch,
-             m._binding.LAYOUT_CODE[case.layout], case.sparse_mode, case.init_blocks,
+             case.block_size, m._binding.LAYOUT_CODE[case.layout], case.sparse_mode,
+             case.init_blocks,
              case.local_blocks, case.local_mode, ctypes.c_void_p(out.data_ptr()), W,
              ctypes.c_void_p(stream.cuda_stream), family)
         calls.append(a)

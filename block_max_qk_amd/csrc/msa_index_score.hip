@@ -1,7 +1,9 @@
 // Host side of the msa_index_score C ABI (and of msa_block_topk, the top-k
 // selection over its output): argument validation (all of it before any HIP
 // call), work planning, and the launch of one gfx950 kernel on the caller's
-// stream.  The library allocates nothing and keeps no state.
+// stream.  The library allocates nothing; the only state it keeps is one
+// figure per device and key type, the decode kernel's workgroup slot count,
+// looked up on the first decode launch there.
 #include "msa_index_score.h"
 
 #include <hip/hip_runtime.h>
@@ -9,6 +11,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <tuple>
 
 #include "msa_kernels.hpp"
 #include "msa_topk.hpp"
@@ -60,12 +63,26 @@ int32_t choose_family(int64_t T, int32_t B, int32_t g) {
   return rows >= (int64_t)(msa::kPrefillRows / 2) * std::max<int32_t>(B, 1) ? 1 : 0;
 }
 
+// Launch `kern` with these arguments (converted to its parameter types) and
+// return the status of this launch alone.  (hipGetLastError after a
+// triple-chevron launch would also return, and clear, an error left pending
+// by earlier unrelated HIP calls of the caller.)
+template <typename... KA, typename... A>
+hipError_t launch_kernel(void (*kern)(KA...), dim3 grid, dim3 block, hipStream_t s, A... a) {
+  static_assert(sizeof...(KA) == sizeof...(A), "one value per kernel parameter");
+  std::tuple<KA...> vals{static_cast<KA>(a)...};
+  void* ptrs[sizeof...(KA)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, 0, s);
+}
+
 template <int KK>
 hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
-  if (family == 1) {
-    hipLaunchKernelGGL(msa::prefill_kernel<KK>, dim3((unsigned)prefill_grid), dim3(256), 0, s, p);
-    return hipGetLastError();
-  }
+  if (family == 1)
+    return launch_kernel(msa::prefill_kernel<KK>, dim3((unsigned)prefill_grid), dim3(256), s, p);
   // Decode: one round of workgroups, as many as fit on the device at once,
   // split evenly over the units (KV head x head chunk).  The device's slot
   // count for this kernel is looked up once per device (the runtime queries
@@ -87,15 +104,14 @@ hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
     if (cached) slots_of[dev].store(slots, std::memory_order_relaxed);
   }
   const int64_t gu = std::max<int64_t>(1, slots / p.units);
-  hipLaunchKernelGGL(msa::decode_kernel<KK>, dim3((unsigned)(gu * p.units)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(msa::decode_kernel<KK>, dim3((unsigned)(gu * p.units)), dim3(256), s, p);
 }
 
 msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32_t* start_loc,
                  const int32_t* block_table, int64_t max_blocks, const float* scale,
                  const uint8_t* q_mx, const uint8_t* k_mx,
                  const int32_t* cu_seqlens_q, const int32_t* kv_len, int32_t batch,
-                 int32_t layout, int32_t sparse_mode, int32_t init_blocks,
+                 int32_t block_size, int32_t layout, int32_t sparse_mode, int32_t init_blocks,
                  int32_t local_blocks, int32_t local_mode, float* out, int64_t out_width,
                  void* stream, int32_t family, bool mx_entry) {
   // Pointers that a call with no requests (B = 0) or no query tokens (T = 0)
@@ -125,6 +141,9 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   if (query->ndim != 3) return MSA_ERR_SHAPE;
   const int64_t T = query->shape[0], Hq = query->shape[1], D = query->shape[2];
   if (T < 0 || Hq < 1 || D != DB) return MSA_ERR_SHAPE;
+  // the logical block is the page: 128 tokens (guide, section 四: block_size
+  // 128; a paged key's P axis must match it)
+  if (block_size != msa::kP) return MSA_ERR_SHAPE;
   if (is_mx && T > 0 && (!q_mx || !k_mx)) return MSA_ERR_NULL;
   if (!compact_axis(D, query->stride[2], 1) || !compact_axis(Hq, query->stride[1], D) ||
       !compact_axis(T, query->stride[0], Hq * D))
@@ -302,36 +321,38 @@ msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
                              const int32_t* start_loc, const int32_t* block_table,
                              int64_t max_blocks, const float* scale,
                              const int32_t* cu_seqlens_q, const int32_t* kv_len,
-                             int32_t batch, int32_t layout, int32_t sparse_mode,
-                             int32_t init_blocks, int32_t local_blocks, float* out,
-                             int64_t out_width, void* stream) {
+                             int32_t batch, int32_t block_size, int32_t layout,
+                             int32_t sparse_mode, int32_t init_blocks, int32_t local_blocks,
+                             float* out, int64_t out_width, void* stream) {
   return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
-             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             MSA_LOCAL_PER_REQUEST, out, out_width, stream, -1, false);
+             cu_seqlens_q, kv_len, batch, block_size, layout, sparse_mode, init_blocks,
+             local_blocks, MSA_LOCAL_PER_REQUEST, out, out_width, stream, -1, false);
 }
 
 msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_t* key,
                                     const int32_t* start_loc, const int32_t* block_table,
                                     int64_t max_blocks, const float* scale,
                                     const int32_t* cu_seqlens_q, const int32_t* kv_len,
-                                    int32_t batch, int32_t layout, int32_t sparse_mode,
-                                    int32_t init_blocks, int32_t local_blocks, float* out,
-                                    int64_t out_width, void* stream, int32_t family) {
+                                    int32_t batch, int32_t block_size, int32_t layout,
+                                    int32_t sparse_mode, int32_t init_blocks,
+                                    int32_t local_blocks, float* out, int64_t out_width,
+                                    void* stream, int32_t family) {
   return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
-             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             MSA_LOCAL_PER_REQUEST, out, out_width, stream, family, false);
+             cu_seqlens_q, kv_len, batch, block_size, layout, sparse_mode, init_blocks,
+             local_blocks, MSA_LOCAL_PER_REQUEST, out, out_width, stream, family, false);
 }
 
 msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* key,
                                 const int32_t* start_loc, const int32_t* block_table,
                                 int64_t max_blocks, const float* scale,
                                 const int32_t* cu_seqlens_q, const int32_t* kv_len,
-                                int32_t batch, int32_t layout, int32_t sparse_mode,
-                                int32_t init_blocks, int32_t local_blocks, int32_t local_mode,
-                                float* out, int64_t out_width, void* stream, int32_t family) {
+                                int32_t batch, int32_t block_size, int32_t layout,
+                                int32_t sparse_mode, int32_t init_blocks, int32_t local_blocks,
+                                int32_t local_mode, float* out, int64_t out_width, void* stream,
+                                int32_t family) {
   return run(query, key, start_loc, block_table, max_blocks, scale, nullptr, nullptr,
-             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             local_mode, out, out_width, stream, family, false);
+             cu_seqlens_q, kv_len, batch, block_size, layout, sparse_mode, init_blocks,
+             local_blocks, local_mode, out, out_width, stream, family, false);
 }
 
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
@@ -356,15 +377,12 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   const int R = many ? 2 : 1;
   const dim3 grid((unsigned)((T + msa::kTopkWaves * R - 1) / (msa::kTopkWaves * R)), (unsigned)Hq);
   const dim3 block(64 * msa::kTopkWaves);
-#define MSA_TOPK_LAUNCH(J)                                                                         \
-  do {                                                                                             \
-    if (many)                                                                                      \
-      hipLaunchKernelGGL((msa::topk_kernel<J, 2>), grid, block, 0, s, scores, T, Hq, width, nv, k,  \
-                         out);                                                                     \
-    else                                                                                           \
-      hipLaunchKernelGGL((msa::topk_kernel<J, 1>), grid, block, 0, s, scores, T, Hq, width, nv, k,  \
-                         out);                                                                     \
-  } while (0)
+  hipError_t e;
+#define MSA_TOPK_LAUNCH(J)                                                                        \
+  e = many ? launch_kernel(msa::topk_kernel<J, 2>, grid, block, s, scores, T, Hq, width, nv, k,   \
+                           out)                                                                   \
+           : launch_kernel(msa::topk_kernel<J, 1>, grid, block, s, scores, T, Hq, width, nv, k,   \
+                           out)
   if (nv <= 128)
     MSA_TOPK_LAUNCH(2);
   else if (nv <= 256)
@@ -376,39 +394,40 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   else if (nv <= 2048)
     MSA_TOPK_LAUNCH(32);
   else
-    hipLaunchKernelGGL((msa::topk_kernel<0, 1>), grid, block, 0, s, scores, T, Hq, width, nv, k, out);
+    e = launch_kernel(msa::topk_kernel<0, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
 #undef MSA_TOPK_LAUNCH
-  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
+  return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* query_scale,
                                    const msa_tensor_t* key, const uint8_t* key_scale,
                                    const int32_t* start_loc, const int32_t* block_table,
                                    int64_t max_blocks, const int32_t* cu_seqlens_q,
-                                   const int32_t* kv_len, int32_t batch, int32_t layout,
-                                   int32_t sparse_mode, int32_t init_blocks,
+                                   const int32_t* kv_len, int32_t batch, int32_t block_size,
+                                   int32_t layout, int32_t sparse_mode, int32_t init_blocks,
                                    int32_t local_blocks, int32_t local_mode, float* out,
                                    int64_t out_width, void* stream) {
   if (!query || !key) return MSA_ERR_NULL;
   if (query->dtype != MSA_DTYPE_MXFP4 || key->dtype != MSA_DTYPE_MXFP4) return MSA_ERR_DTYPE;
   return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
-             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             local_mode, out, out_width, stream, -1, true);
+             cu_seqlens_q, kv_len, batch, block_size, layout, sparse_mode, init_blocks,
+             local_blocks, local_mode, out, out_width, stream, -1, true);
 }
 
 msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8_t* query_scale,
                                           const msa_tensor_t* key, const uint8_t* key_scale,
                                           const int32_t* start_loc, const int32_t* block_table,
                                           int64_t max_blocks, const int32_t* cu_seqlens_q,
-                                          const int32_t* kv_len, int32_t batch, int32_t layout,
+                                          const int32_t* kv_len, int32_t batch,
+                                          int32_t block_size, int32_t layout,
                                           int32_t sparse_mode, int32_t init_blocks,
                                           int32_t local_blocks, int32_t local_mode, float* out,
                                           int64_t out_width, void* stream, int32_t family) {
   if (!query || !key) return MSA_ERR_NULL;
   if (query->dtype != MSA_DTYPE_MXFP4 || key->dtype != MSA_DTYPE_MXFP4) return MSA_ERR_DTYPE;
   return run(query, key, start_loc, block_table, max_blocks, nullptr, query_scale, key_scale,
-             cu_seqlens_q, kv_len, batch, layout, sparse_mode, init_blocks, local_blocks,
-             local_mode, out, out_width, stream, family, true);
+             cu_seqlens_q, kv_len, batch, block_size, layout, sparse_mode, init_blocks,
+             local_blocks, local_mode, out, out_width, stream, family, true);
 }
 
 int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }

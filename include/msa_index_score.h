@@ -109,7 +109,14 @@ typedef struct {
  * cu_seqlens_q device int32 [B+1], cu_seqlens_q[0] = 0, non-decreasing,
  *              cu_seqlens_q[B] = T.
  * kv_len       device int32 [B], visible KV length of each request (for TND
- *              the requests' keys are packed back to back in this order).
+ *              the requests' keys are packed back to back in this order;
+ *              the guide's TND actual_seq_klen is the [B+1] prefix sum of
+ *              these lengths, which the caller differences first).
+ * batch        B, the number of requests (>= 0; 0 only when T = 0).
+ * block_size   tokens per logical block, which is also a paged key's P axis
+ *              (guide, section 四: the kernel splits every request's keys into
+ *              blocks of block_size = 128); must be 128 (MSA_ERR_SHAPE
+ *              otherwise).
  * layout       msa_layout_t.
  * sparse_mode  3 (right-down causal) or 0 (no causal mask).
  * init_blocks, local_blocks
@@ -129,8 +136,12 @@ typedef struct {
  * block_table when batch = 0, and out when T = 0.
  *
  * Ownership: every pointer is caller-owned; the library allocates no device
- * memory and keeps no state between calls.  Returns MSA_OK or an error
- * status; T = 0 returns MSA_OK without launching anything.  query, key and
+ * memory.  The only state it keeps between calls is one figure per device
+ * and key type: the decode kernel's workgroup slot count (CU count times
+ * occupancy), asked of the HIP runtime on the first decode launch on that
+ * device.  Returns MSA_OK or an error status; T = 0 returns MSA_OK without
+ * launching anything.  MSA_ERR_HIP reports a failure of this call's own
+ * runtime queries or launch, never an error pending from earlier HIP work.  query, key and
  * out must be 16-byte aligned and a paged key's dim0 stride a multiple of 16
  * bytes (MSA_ERR_STRIDE otherwise).  Sizes past the kernels' 32-bit indexing
  * return MSA_ERR_SHAPE: out_width > 2^24, Hq > 2^16, batch > 2^30, T >= 2^31,
@@ -140,9 +151,9 @@ msa_status_t msa_index_score(const msa_tensor_t* query, const msa_tensor_t* key,
                              const int32_t* start_loc, const int32_t* block_table,
                              int64_t max_blocks, const float* scale,
                              const int32_t* cu_seqlens_q, const int32_t* kv_len,
-                             int32_t batch, int32_t layout, int32_t sparse_mode,
-                             int32_t init_blocks, int32_t local_blocks, float* out,
-                             int64_t out_width, void* stream);
+                             int32_t batch, int32_t block_size, int32_t layout,
+                             int32_t sparse_mode, int32_t init_blocks, int32_t local_blocks,
+                             float* out, int64_t out_width, void* stream);
 
 /* Same as msa_index_score, with the kernel family chosen by the caller:
  * family = -1 picks it from the sizes (as msa_index_score does), 0 forces the
@@ -153,9 +164,10 @@ msa_status_t msa_index_score_family(const msa_tensor_t* query, const msa_tensor_
                                     const int32_t* start_loc, const int32_t* block_table,
                                     int64_t max_blocks, const float* scale,
                                     const int32_t* cu_seqlens_q, const int32_t* kv_len,
-                                    int32_t batch, int32_t layout, int32_t sparse_mode,
-                                    int32_t init_blocks, int32_t local_blocks, float* out,
-                                    int64_t out_width, void* stream, int32_t family);
+                                    int32_t batch, int32_t block_size, int32_t layout,
+                                    int32_t sparse_mode, int32_t init_blocks,
+                                    int32_t local_blocks, float* out, int64_t out_width,
+                                    void* stream, int32_t family);
 
 /* Same as msa_index_score_family, with the local_mask window's placement
  * chosen by local_mode (msa_local_mode_t; any other value returns
@@ -167,9 +179,10 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
                                 const int32_t* start_loc, const int32_t* block_table,
                                 int64_t max_blocks, const float* scale,
                                 const int32_t* cu_seqlens_q, const int32_t* kv_len,
-                                int32_t batch, int32_t layout, int32_t sparse_mode,
-                                int32_t init_blocks, int32_t local_blocks, int32_t local_mode,
-                                float* out, int64_t out_width, void* stream, int32_t family);
+                                int32_t batch, int32_t block_size, int32_t layout,
+                                int32_t sparse_mode, int32_t init_blocks, int32_t local_blocks,
+                                int32_t local_mode, float* out, int64_t out_width, void* stream,
+                                int32_t family);
 
 /* The block score on MXFP4 index vectors: the FP4 indexer variant of the
  * notes "MiniMax Sparse Attention: paper algorithm and code" (section 4.6,
@@ -206,8 +219,8 @@ msa_status_t msa_index_score_mxfp4(const msa_tensor_t* query, const uint8_t* que
                                    const msa_tensor_t* key, const uint8_t* key_scale,
                                    const int32_t* start_loc, const int32_t* block_table,
                                    int64_t max_blocks, const int32_t* cu_seqlens_q,
-                                   const int32_t* kv_len, int32_t batch, int32_t layout,
-                                   int32_t sparse_mode, int32_t init_blocks,
+                                   const int32_t* kv_len, int32_t batch, int32_t block_size,
+                                   int32_t layout, int32_t sparse_mode, int32_t init_blocks,
                                    int32_t local_blocks, int32_t local_mode, float* out,
                                    int64_t out_width, void* stream);
 
@@ -219,7 +232,8 @@ msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8
                                           const msa_tensor_t* key, const uint8_t* key_scale,
                                           const int32_t* start_loc, const int32_t* block_table,
                                           int64_t max_blocks, const int32_t* cu_seqlens_q,
-                                          const int32_t* kv_len, int32_t batch, int32_t layout,
+                                          const int32_t* kv_len, int32_t batch,
+                                          int32_t block_size, int32_t layout,
                                           int32_t sparse_mode, int32_t init_blocks,
                                           int32_t local_blocks, int32_t local_mode, float* out,
                                           int64_t out_width, void* stream, int32_t family);

@@ -80,15 +80,16 @@ def tdesc(shape, stride=None, dtype=0, addr=FAKE):
 
 
 def call(q=None, k=None, *, start=FAKE, table=FAKE, mb=2, scale=None, cu=FAKE, kv=FAKE, B=1,
-         layout=1, mode=3, init=0, local=1, out=FAKE, width=16, family=None, local_mode=None):
+         bs=128, layout=1, mode=3, init=0, local=1, out=FAKE, width=16, family=None,
+         local_mode=None):
     lib = m.load_library()
     q = q if q is not None else tdesc([32, 8, 128], dtype=DT["f16"])
     k = k if k is not None else tdesc([8, 128, 1, 128], dtype=DT["f16"])
     args = [ctypes.byref(q) if q is not False else None,
             ctypes.byref(k) if k is not False else None,
-            start, table, mb, scale, cu, kv, B, layout, mode, init, local, out, width, None]
+            start, table, mb, scale, cu, kv, B, bs, layout, mode, init, local, out, width, None]
     if local_mode is not None:
-        return lib.msa_index_score_ex(*args[:13], local_mode, *args[13:],
+        return lib.msa_index_score_ex(*args[:14], local_mode, *args[14:],
                                       -1 if family is None else family)
     if family is None:
         return lib.msa_index_score(*args)
@@ -225,13 +226,13 @@ def test_local_mode_rules():
 
 
 def mx_call(q=None, k=None, *, qs=FAKE, ks=FAKE, start=FAKE, table=FAKE, mb=2, cu=FAKE,
-            kv=FAKE, B=1, layout=1, mode=3, init=0, local=1, local_mode=0, out=FAKE, width=16,
-            family=None):
+            kv=FAKE, B=1, bs=128, layout=1, mode=3, init=0, local=1, local_mode=0, out=FAKE,
+            width=16, family=None):
     lib = m.load_library()
     q = q if q is not None else tdesc([32, 8, 64], dtype=5)
     k = k if k is not None else tdesc([8, 128, 1, 64], dtype=5)
-    args = (ctypes.byref(q), qs, ctypes.byref(k), ks, start, table, mb, cu, kv, B, layout, mode,
-            init, local, local_mode, out, width, None)
+    args = (ctypes.byref(q), qs, ctypes.byref(k), ks, start, table, mb, cu, kv, B, bs, layout,
+            mode, init, local, local_mode, out, width, None)
     if family is None:
         return lib.msa_index_score_mxfp4(*args)
     return lib.msa_index_score_mxfp4_family(*args, family)
@@ -294,3 +295,159 @@ def test_block_topk_binding_checks_shapes():
         m.msa_block_topk(s, 16, 16, torch.zeros(3, 2, 8, dtype=torch.int32))
     with pytest.raises(ValueError):
         m.msa_block_topk(s.double(), 16, 16, torch.zeros(3, 2, 16, dtype=torch.int32))
+
+
+def test_block_size_must_be_128():
+    # The logical block is the 128-token page (guide, section 四); every score
+    # entry takes block_size and rejects any other value before launching.
+    q0 = tdesc([0, 8, 128], dtype=0)
+    assert call(q=q0) == OK
+    for bs in (0, 64, 127, 129, 256):
+        assert call(q=q0, bs=bs) == SHAPE
+        assert call(q=q0, bs=bs, local_mode=1) == SHAPE
+        assert call(q=q0, bs=bs, family=0) == SHAPE
+        assert mx_call(q=tdesc([0, 8, 64], dtype=5), bs=bs) == SHAPE
+        assert mx_call(q=tdesc([0, 8, 64], dtype=5), bs=bs, family=1) == SHAPE
+
+
+# ---------------------------------------------------------------------------
+# the Python wrappers: sizes the C ABI cannot see, and the guide's keyword API
+# ---------------------------------------------------------------------------
+
+def _cpu_args(B=2, T=0, Hq=8, mb=4):
+    """Host tensors for a paged fp16 call with T query tokens (T = 0 never
+    launches)."""
+    return dict(query=torch.zeros(T, Hq, 128, dtype=torch.float16),
+                key=torch.zeros(8, 128, 1, 128, dtype=torch.float16),
+                start_loc=torch.zeros(B, dtype=torch.int32),
+                block_table=torch.zeros(B, mb, dtype=torch.int32), scale=None,
+                cu_seqlens_q=torch.zeros(B + 1, dtype=torch.int32),
+                kv_len=torch.ones(B, dtype=torch.int32), layout="BBND", sparse_mode=3,
+                init_blocks=0, local_blocks=1,
+                out=torch.empty(Hq, T, m.msa_index_score_out_width(mb)), max_blocks=mb,
+                stream=0)
+
+
+def test_wrapper_accepts_consistent_sizes():
+    m.msa_index_score(**_cpu_args())       # T = 0: validated, nothing launched
+
+
+@pytest.mark.parametrize("change,what", [
+    (dict(cu_seqlens_q=torch.zeros(2, dtype=torch.int32)), "cu_seqlens_q"),    # not [B+1]
+    (dict(cu_seqlens_q=torch.zeros(4, dtype=torch.int32)), "cu_seqlens_q"),
+    (dict(start_loc=torch.zeros(3, dtype=torch.int32)), "start_loc"),          # not [B]
+    (dict(start_loc=None), "start_loc"),                                       # per-request window
+    (dict(block_table=torch.zeros(1, 4, dtype=torch.int32)), "block_table"),  # fewer rows than B
+    (dict(block_table=torch.zeros(2, 5, dtype=torch.int32)), "block_table"),  # width != MB
+    (dict(kv_len=torch.ones(2, 1, dtype=torch.int32)), "kv_len"),             # not 1-D
+    (dict(out=torch.empty(4, 0, 16)), "out"),                                  # Hq mismatch
+    (dict(out=torch.empty(8, 3, 16)), "out"),                                  # T mismatch
+])
+def test_wrapper_rejects_inconsistent_sizes(change, what):
+    a = _cpu_args()
+    a.update(change)
+    with pytest.raises(ValueError, match=what):
+        m.msa_index_score(**a)
+
+
+def test_wrapper_start_loc_optional_per_query():
+    a = _cpu_args()
+    a.update(start_loc=None, local_mode="query")
+    m.msa_index_score(**a)
+
+
+def test_wrapper_scale_size():
+    a = _cpu_args()
+    a.update(query=torch.zeros(0, 8, 128, dtype=torch.float16),
+             key=torch.zeros(8, 1, 128, 128, dtype=torch.int8), layout="BNBD")
+    a["scale"] = torch.ones(8, 1, 128)                 # [NP, Hkv, P]: one per token and head
+    m.msa_index_score(**a)
+    a["scale"] = torch.ones(8, 1, 64)
+    with pytest.raises(ValueError, match="scale"):
+        m.msa_index_score(**a)
+
+
+def test_mxfp4_wrapper_sizes():
+    B, mb = 2, 4
+    base = dict(query=torch.zeros(0, 8, 64, dtype=torch.uint8),
+                query_scale=torch.zeros(0, 8, 4, dtype=torch.uint8),
+                key=torch.zeros(8, 128, 1, 64, dtype=torch.uint8),
+                key_scale=torch.zeros(8, 128, 1, 4, dtype=torch.uint8),
+                start_loc=torch.zeros(B, dtype=torch.int32),
+                block_table=torch.zeros(B, mb, dtype=torch.int32),
+                cu_seqlens_q=torch.zeros(B + 1, dtype=torch.int32),
+                kv_len=torch.ones(B, dtype=torch.int32), layout="BBND", sparse_mode=3,
+                init_blocks=0, local_blocks=1, out=torch.empty(8, 0, 16), max_blocks=mb,
+                stream=0)
+    m.msa_index_score_mxfp4(**base)
+    for change, what in ((dict(key_scale=torch.zeros(8, 128, 1, 2, dtype=torch.uint8)),
+                          "key_scale"),
+                         (dict(query=torch.zeros(1, 8, 64, dtype=torch.uint8),
+                               query_scale=torch.zeros(1, 8, 2, dtype=torch.uint8),
+                               out=torch.empty(8, 1, 16)), "query_scale"),
+                         (dict(cu_seqlens_q=torch.zeros(B, dtype=torch.int32)), "cu_seqlens_q"),
+                         (dict(block_table=torch.zeros(B, mb + 1, dtype=torch.int32)),
+                          "block_table")):
+        a = dict(base, **change)
+        with pytest.raises(ValueError, match=what):
+            m.msa_index_score_mxfp4(**a)
+
+
+def _guide_args(**kw):
+    a = dict(block_table=torch.zeros(1, 2, dtype=torch.int32),
+             atten_mask=torch.zeros(2048, 2048, dtype=torch.int8),
+             actual_seq_qlen=torch.tensor([0, 0], dtype=torch.int32),
+             actual_seq_klen=torch.tensor([256], dtype=torch.int32), stream=0)
+    a.update(kw)
+    return (torch.zeros(0, 8, 128, dtype=torch.float16),
+            torch.zeros(8, 128, 1, 128, dtype=torch.float16),
+            torch.tensor([1], dtype=torch.int32)), a
+
+
+def test_guide_api_atten_mask_rules():
+    # guide, sections 四 and 十: sparse_mode 3 takes the [2048, 2048] int8
+    # template, sparse_mode 0 none; the host checks it, the device never reads it
+    pos, kw = _guide_args()
+    out = m.index_score(*pos, **kw)
+    assert tuple(out.shape) == (8, 0, 16)
+    for bad in (None, torch.zeros(2048, 2048, dtype=torch.bool),
+                torch.zeros(1024, 2048, dtype=torch.int8)):
+        pos, kw = _guide_args(atten_mask=bad)
+        with pytest.raises(ValueError, match="atten_mask"):
+            m.index_score(*pos, **kw)
+    pos, kw = _guide_args(sparse_mode=0)
+    with pytest.raises(ValueError, match="atten_mask"):
+        m.index_score(*pos, **kw)
+    pos, kw = _guide_args(sparse_mode=0, atten_mask=None)
+    m.index_score(*pos, **kw)
+
+
+def test_guide_api_tnd_prefix_sum(monkeypatch):
+    # guide, section 四 and 6.3: a TND actual_seq_klen is the [B+1] prefix sum
+    # of the packed key; the wrapper passes per-request lengths to the C ABI
+    # and takes MB as the largest ceil(length / 128).
+    seen = {}
+
+    def spy(*a, **k):
+        seen["kv_len"] = a[6].clone()
+        seen["max_blocks"] = a[12]
+        return a[11]
+
+    monkeypatch.setattr(m._binding, "msa_index_score", spy)
+    q = torch.zeros(0, 8, 128, dtype=torch.float16)
+    key = torch.zeros(2200, 1, 128, dtype=torch.float16)
+    out = m.index_score(q, key, torch.zeros(2, dtype=torch.int32),
+                        atten_mask=torch.zeros(2048, 2048, dtype=torch.int8),
+                        actual_seq_qlen=torch.zeros(3, dtype=torch.int32),
+                        actual_seq_klen=torch.tensor([0, 2100, 2200], dtype=torch.int32),
+                        layout_key="tnd", stream=0)
+    assert seen["kv_len"].tolist() == [2100, 100]
+    assert seen["kv_len"].dtype == torch.int32
+    assert seen["max_blocks"] == 17 and tuple(out.shape) == (8, 0, 32)
+    # an empty batch falls back to ceil(T2 / 128)
+    m.index_score(q, key, torch.zeros(0, dtype=torch.int32),
+                  atten_mask=torch.zeros(2048, 2048, dtype=torch.int8),
+                  actual_seq_qlen=torch.zeros(1, dtype=torch.int32),
+                  actual_seq_klen=torch.tensor([0], dtype=torch.int32), layout_key="TND",
+                  stream=0)
+    assert seen["max_blocks"] == (2200 + 127) // 128
