@@ -279,8 +279,10 @@ static int check(orc_args* a) {
     acc += a->kv_len[b];
     int64_t NB = ceil_div(a->kv_len[b], a->P);
     if (NB > a->W) return -4;
+    /* every layout: MB is the largest block count (paged: the table width;
+       packed: max ceil(kv_len/P), guide section 五) */
+    if (NB > a->MB) return -5;
     if (a->layout != ORC_TND) {
-      if (NB > a->MB) return -5;
       for (int64_t beta = 0; beta < NB; ++beta) {
         int32_t p = a->block_table[(int64_t)b * a->MB + beta];
         if (p < 0 || p >= a->k_dim0) return -6;

@@ -371,6 +371,19 @@ def test_contract_violation_raises():
         oracle.index_score_case(bad)
 
 
+def test_packed_key_block_count_above_max_blocks_raises():
+    # Packed (TND) keys: MB is the largest ceil(kv_len / 128) of the batch
+    # (guide, section 五), so a request with more blocks than MB breaks the
+    # contract even when its blocks would still fit the aligned width.
+    c = synth.make_case("tnd_mb", 52, q_lens=[2, 3], kv_lens=[300, 700], Hq=2, Hkv=1,
+                        qdtype="bf16", layout="TND")
+    assert c.max_blocks == 6
+    oracle.index_score_case(c)                     # NB = 3 and 6: within MB
+    for mb in (5, 3):                              # W stays 16 > NB = 6
+        with pytest.raises(ValueError):
+            oracle.index_score_case(dataclasses.replace(c, max_blocks=mb))
+
+
 # ---------------------------------------------------------------------------
 # MXFP4 element and scale decoders
 # ---------------------------------------------------------------------------
