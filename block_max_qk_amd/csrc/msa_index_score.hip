@@ -56,11 +56,40 @@ bool compact_axis(int64_t extent, int64_t stride, int64_t want) {
   return extent <= 1 || stride == want;
 }
 
-int32_t choose_family(int64_t T, int32_t B, int32_t g) {
-  // Prefill tiles pay off once requests carry about half a 256-row tile of
-  // query rows on average; shorter query runs use 16-row decode tiles.
+// Kernel family.  Prefill tiles (hundreds of rows sharing each key block
+// staged in LDS) pay off once requests carry about half a 256-row tile of
+// query rows on average and the batch holds a few tiles' worth of rows in all
+// (T * Hq >= 1024); otherwise the 16-row decode tiles, whose (tile, block)
+// work list spreads even one short request over the whole chip.  Measured on
+// one paged bf16 request (B = 1, Hkv = 1): 32 tokens x 8 heads, 2 blocks,
+// 7.9 us on decode tiles against 13.0 us on one prefill tile; with 16384
+// keys, 64 tokens x 8 heads, 16.6 against 112 us; from 1024 tokens x 8
+// heads on, prefill tiles win at every kv length tried (256 to 16384).
+int32_t choose_family(int64_t T, int32_t B, int32_t Hq, int32_t Hkv) {
+  const int64_t g = std::max<int32_t>(Hq / std::max<int32_t>(Hkv, 1), 1);
   const int64_t rows = T * std::min<int64_t>(g, msa::kPrefillRows);
-  return rows >= (int64_t)(msa::kPrefillRows / 2) * std::max<int32_t>(B, 1) ? 1 : 0;
+  const bool long_runs = rows >= (int64_t)(msa::kPrefillRows / 2) * std::max<int32_t>(B, 1);
+  return long_runs && T * (int64_t)Hq >= 1024 ? 1 : 0;
+}
+
+// Blocks per prefill work item.  The key type's default (msa_kernels.hpp,
+// prefill_chunk) amortises a work item's set-up over many blocks; when that
+// leaves fewer than kPrefillMinItems work items for the whole launch, the
+// chunk shrinks (to a multiple of 4 blocks, at least 4: the kernels write a
+// row's columns in aligned groups of 4) until the items cover the chip: one
+// workgroup per work item runs its blocks in sequence, so a short prefill of
+// a long context would otherwise take tens of blocks per workgroup on a few
+// dozen CUs.  Measured on one bf16 request of 16384 keys, 256 tokens x 8
+// heads: 113 us with 40-block items, 30 us with 8-block ones.
+constexpr int64_t kPrefillMinItems = 1024;
+
+int32_t prefill_chunk_for(int32_t dflt, int64_t W, int64_t units_per_chunk, int64_t ntiles) {
+  const int64_t per_chunk = std::max<int64_t>(units_per_chunk * ntiles, 1);
+  if (per_chunk * ((W + dflt - 1) / dflt) >= kPrefillMinItems) return dflt;
+  const int64_t want = (kPrefillMinItems + per_chunk - 1) / per_chunk;   // chunks per row
+  int64_t c = (W + want - 1) / want;
+  c = (c + 3) / 4 * 4;
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(c, 4), dflt);
 }
 
 // Launch `kern` with these arguments (converted to its parameter types) and
@@ -239,7 +268,7 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
 
   // plan
   const int32_t g = (int32_t)(Hq / Hkv);
-  const int fam = family >= 0 ? family : choose_family(T, batch, g);
+  const int fam = family >= 0 ? family : choose_family(T, batch, (int32_t)Hq, (int32_t)Hkv);
   const int rows = fam == 1 ? msa::prefill_rows(is_mx ? msa::KMXFP4 : key->dtype)
                             : msa::kDecodeRows;
   Params p{};
@@ -291,11 +320,12 @@ msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32
   p.hchunks = (g + p.hpt - 1) / p.hpt;
   // prefill units: (KV head, head chunk, block chunk); decode units: (KV
   // head, head chunk), each walking its own copy of the batch's work list
-  p.chunk = msa::prefill_chunk(is_mx ? msa::KMXFP4 : key->dtype);
-  p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
-  p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t bound = (T + (int64_t)batch * (p.tpt - 1)) / p.tpt;
   p.ntiles = (int32_t)std::min<int64_t>(T, bound);
+  p.chunk = msa::prefill_chunk(is_mx ? msa::KMXFP4 : key->dtype);
+  if (fam == 1) p.chunk = prefill_chunk_for(p.chunk, W, (int64_t)p.Hkv * p.hchunks, p.ntiles);
+  p.nchunks = fam == 1 ? (int32_t)((W + p.chunk - 1) / p.chunk) : 1;
+  p.units = p.Hkv * p.hchunks * p.nchunks;
   const int64_t units8 = ((int64_t)p.units + 7) / 8 * 8;
   const int64_t grid = units8 * p.ntiles;
   if (grid > INT32_MAX || (int64_t)p.units * p.ntiles > INT32_MAX) return MSA_ERR_SHAPE;
@@ -433,8 +463,7 @@ msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8
 int64_t msa_index_score_out_width(int64_t max_blocks) { return round_up16(max_blocks); }
 
 int32_t msa_index_score_kernel_family(int64_t T, int32_t batch, int32_t Hq, int32_t Hkv) {
-  if (Hkv < 1) Hkv = 1;
-  return choose_family(T, batch, std::max<int32_t>(Hq / Hkv, 1));
+  return choose_family(T, batch, Hq, Hkv);
 }
 
 const char* msa_status_str(int32_t s) {

@@ -277,7 +277,9 @@ const char* msa_status_str(int32_t status);
 
 /* Which kernel family a call with these sizes would use: 0 = decode tiles
  * (16 query rows per tile, for short query runs per request), 1 = prefill
- * tiles (256 query rows per tile).  Host-only; for benchmarks and tests. */
+ * tiles (hundreds of query rows per tile), chosen when requests average at
+ * least 128 query rows (tokens times heads per KV group) and the batch has
+ * at least 1024 (T * Hq).  Host-only; for benchmarks and tests. */
 int32_t msa_index_score_kernel_family(int64_t T, int32_t batch, int32_t Hq, int32_t Hkv);
 
 #ifdef __cplusplus

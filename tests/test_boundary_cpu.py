@@ -53,7 +53,14 @@ def test_kernel_family_choice():
     assert m.msa_index_score_kernel_family(32, 32, 16, 1) == 0        # int8 decode batch
     assert m.msa_index_score_kernel_family(15360, 4, 32, 4) == 1      # varlen prefill
     assert m.msa_index_score_kernel_family(4096, 1, 64, 8) == 1       # chunked prefill
-    assert m.msa_index_score_kernel_family(32, 1, 8, 1) == 1          # tiny prefill
+    # one short request: 32 or 64 tokens x 8 heads spread further as 16-row
+    # decode tiles than as one prefill tile; from 1024 query rows on, prefill
+    assert m.msa_index_score_kernel_family(32, 1, 8, 1) == 0          # the guide's tiny example
+    assert m.msa_index_score_kernel_family(64, 1, 8, 1) == 0
+    assert m.msa_index_score_kernel_family(128, 1, 8, 1) == 1
+    assert m.msa_index_score_kernel_family(64, 1, 16, 1) == 1
+    assert m.msa_index_score_kernel_family(1024, 8, 8, 1) == 1
+    assert m.msa_index_score_kernel_family(1024, 128, 8, 1) == 0      # 8 tokens per request
 
 
 # ---------------------------------------------------------------------------
