@@ -14,8 +14,15 @@ duration for the roofline.
 To keep the 256 MB Infinity Cache from serving repeated reads, the key cache
 is replicated into several HBM copies and the steps rotate over them.
 
-Output: one JSON line (rank 0 of 1).  ``--config all`` prints one line per
-workload instead (for measurement; the default line is the headline).
+Output: one JSON line (rank 0 of 1).  By default its top level is the
+headline decode batch, and its ``workloads`` list holds all five base
+workloads measured in the same process (the tiny example, the decode batch,
+the varlen prefill, the int8 decode batch and the chunked fp8 prefill), each
+with its average launch duration, roofline (with HBM traffic from the
+committed counter runs when they match the current kernel sources), the
+oracle's CPU baseline on this host's available cores (one core too, for the
+decode-sized ones) and, for the prefill workloads, the top-k selection on
+their scores.  ``--config all`` prints one full line per workload instead.
 ``--topk`` times the top-k block selection (msa_block_topk, k = 16) over the
 chosen workload's score rows instead, with its own roofline (HBM bytes: every
 row's num_valid scores read, its k indices written).  ``--local-mode query``
@@ -99,7 +106,8 @@ def workload_stats(case) -> dict:
 
 
 def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
-                 cpu_baseline: bool, args, local_mode: int = 0) -> dict:
+                 cpu_baseline: bool, args, local_mode: int = 0, topk: bool = False,
+                 host: dict = None) -> dict:
     import dataclasses
     import torch
     import block_max_qk_amd as m
@@ -227,10 +235,42 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
         "cpu_baseline": None,
         "input_generation_s": round(t_gen, 2),
     }
-    del calls, keep
+    if topk:
+        # the selection that follows the operator, timed on the scores the
+        # last step wrote (resident in HBM)
+        res["topk"] = time_topk(out, case.max_blocks, steps, warmup, stream)
+    del calls, keep, out
     if cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_leg(case, stats, args)
+        res["cpu_baseline"] = cpu_baseline_leg(case, stats, args, host or host_cpu())
     return res
+
+
+def time_topk(scores, num_valid: int, steps: int, warmup: int, stream, k: int = 16) -> dict:
+    """msa_block_topk (k = 16) over every row of a score tensor already in
+    HBM: average launch duration from one event pair around the launches, and
+    its HBM roofline (each row's num_valid scores read, k indices written)."""
+    import torch
+    import block_max_qk_amd as m
+    Hq, T, W = scores.shape
+    out = torch.empty((T, Hq, k), dtype=torch.int32, device=scores.device)
+    for _ in range(warmup):
+        m.msa_block_topk(scores, num_valid, k, out, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        m.msa_block_topk(scores, num_valid, k, out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = Hq * T * (num_valid + k) * 4
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"kernel": "topk_kernel", "k": k, "rows": Hq * T, "num_valid": num_valid,
+            "kernel_ms_avg": round(ms, 5), "selections_per_s": round(Hq * T / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": alg}}
 
 
 def measured_traffic(workload: str):
@@ -246,35 +286,117 @@ def measured_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline_leg(case, stats, args) -> dict:
-    """The CPU oracle, as it is, timed on this host on a bounded sample of the
-    same workload, scaled to block scores/s."""
+def host_cpu() -> dict:
+    """The host the oracle runs on: core counts as the OS reports them, the
+    share this process may use (CPU affinity, cgroup CPU quota and
+    OMP_NUM_THREADS, which a shared GPU host sets to the job's CPU share),
+    and the CPU model."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["affinity"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity"] = os.cpu_count()
+    quota = None
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = round(int(q) / int(per), 2)
+    except (OSError, ValueError):
+        pass
+    info["cgroup_cpus"] = quota
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    info["omp_num_threads"] = int(omp) if omp.isdigit() and int(omp) > 0 else None
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info["cpu_model"] = model
+    avail = info["affinity"] or 1
+    if quota:
+        avail = min(avail, max(1, int(quota)))
+    if info["omp_num_threads"]:
+        avail = min(avail, info["omp_num_threads"])
+    info["cores_available"] = avail
+    return info
+
+
+def visible_blocks_per_token(case):
+    """int64 [T]: blocks with at least one visible key for each query token
+    (the window of workload_stats), i.e. the block scores an (h, t) row costs
+    whatever local_mask later writes over them."""
+    import torch
+    P = case.block_size
+    cu, kv = case.cu_seqlens_q.long(), case.kv_len.long()
+    nvis = torch.zeros(case.T, dtype=torch.int64)
+    for b in range(case.batch):
+        t0, t1, L = int(cu[b]), int(cu[b + 1]), int(kv[b])
+        if t1 == t0 or L == 0:
+            continue
+        i = torch.arange(t1 - t0, dtype=torch.int64)
+        qpos = (L - (t1 - t0) + i) if case.sparse_mode == 3 else torch.full_like(i, L - 1)
+        lim = torch.clamp(torch.minimum(qpos, torch.tensor(L - 1)), min=-1)
+        lim = torch.minimum(lim, torch.tensor(case.max_blocks * P - 1))
+        nvis[t0:t1] = torch.where(lim >= 0, lim // P + 1, torch.zeros_like(lim))
+    return nvis
+
+
+def cpu_baseline_leg(case, stats, args, host: dict) -> dict:
+    """The CPU oracle, as it is, timed on this host's available cores on a
+    bounded sample of the same workload, scaled to block scores/s.  Decode
+    batches and the tiny example: the whole workload on every available core,
+    and one core on the whole tiny example or a random eighth of a batch's
+    requests.  Prefill workloads: whole random output rows on every available
+    core (extrapolated to the workload's rate)."""
     import torch
     import oracle
-    nth = oracle.default_threads()
+    nth = host["cores_available"]
+    W = ((max(case.max_blocks, 1) + 15) // 16) * 16
+    res = {"unit": "block scores/s", "cores": nth, "kind": "oracle", "host": host}
     if case.T <= 256:
         t0 = time.perf_counter()
         oracle.index_score(**oracle.case_args(case), nthreads=nth)
         dt = time.perf_counter() - t0
-        return {"value": round(stats["scores"] / dt, 1), "unit": "block scores/s", "cores": nth,
-                "kind": "oracle", "sample": f"the whole workload ({stats['scores']} block "
-                f"scores) in {dt:.2f} s"}
+        res.update(value=round(stats["scores"] / dt, 1), extrapolated=False,
+                   sample=f"the whole workload ({stats['scores']} block scores) in {dt:.2f} s "
+                          f"on {nth} threads")
+        # one core
+        g = torch.Generator().manual_seed(11)
+        B = case.batch
+        nreq = B if case.T <= 32 else max(1, (B + 7) // 8)
+        reqs = sorted(torch.randperm(B, generator=g)[:nreq].tolist())
+        cu = case.cu_seqlens_q.long()
+        ts = torch.cat([torch.arange(int(cu[b]), int(cu[b + 1])) for b in reqs])
+        hs = torch.arange(case.Hq)
+        pts = torch.stack([hs.repeat_interleave(len(ts) * W), ts.repeat_interleave(W).repeat(case.Hq),
+                           torch.arange(W).repeat(len(ts) * case.Hq)], 1)
+        t0 = time.perf_counter()
+        oracle.index_score_case_points(case, pts, nthreads=1)
+        dt1 = time.perf_counter() - t0
+        n1 = int(visible_blocks_per_token(case)[ts].sum()) * case.Hq
+        res["single_core"] = {"value": round(n1 / dt1, 1), "cores": 1,
+                              "sample": f"{nreq} of {B} requests at random, every entry "
+                                        f"({n1} block scores) in {dt1:.2f} s",
+                              "extrapolated": nreq < B}
+        return res
     # prefill: whole rows (h, t, all blocks) of tokens spread over the batch
     g = torch.Generator().manual_seed(7)
     nrows = args.cpu_rows
     ts = torch.randint(0, case.T, (nrows,), generator=g)
     hs = torch.randint(0, case.Hq, (nrows,), generator=g)
-    W = ((max(case.max_blocks, 1) + 15) // 16) * 16
     beta = torch.arange(W)
     pts = torch.stack([hs.repeat_interleave(W), ts.repeat_interleave(W), beta.repeat(nrows)], 1)
     t0 = time.perf_counter()
-    vals = oracle.index_score_case_points(case, pts, nthreads=nth)
+    oracle.index_score_case_points(case, pts, nthreads=nth)
     dt = time.perf_counter() - t0
-    # block scores of the sampled rows: the finite, non-forced entries
-    sampled = int((torch.isfinite(vals) & (vals.abs() < 1e28)).sum())
-    return {"value": round(sampled / dt, 1), "unit": "block scores/s", "cores": nth,
-            "kind": "oracle", "sample": f"{nrows} whole rows (h, t) at random, {sampled} "
-            f"block scores in {dt:.2f} s"}
+    sampled = int(visible_blocks_per_token(case)[ts].sum())
+    res.update(value=round(sampled / dt, 1), extrapolated=True,
+               sample=f"{nrows} whole rows (h, t) at random, {sampled} block scores in "
+                      f"{dt:.2f} s on {nth} threads, scaled to block scores/s")
+    return res
 
 
 TOPK_METRIC = "top-k block selections/s (k=16) + achieved HBM GB/s, 1 GPU"
@@ -353,21 +475,39 @@ def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) ->
     return res
 
 
+HEADLINE = "decode_bbnd_bf16"
+
+
+def workload_summary(r: dict) -> dict:
+    """One workload's figures for the headline line's 'workloads' list."""
+    keys = ("value", "unit", "ms_per_step", "dtype", "hbm_gbs", "mfma_tflops",
+            "block_scores_per_step", "out_entries_per_step", "roofline", "cpu_baseline", "topk")
+    out = {"workload": r["config"]["workload"], "config": r["config"]}
+    out.update({k: r[k] for k in keys if k in r})
+    out["kernel_ms_avg"] = r["roofline"]["kernel_ms_avg"]
+    out["latency_us"] = round(r["roofline"]["kernel_ms_avg"] * 1e3, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode_bbnd_bf16",
-                    help="workload name or index, 'all' (the five base workloads) or 'mx' "
-                         "(their MXFP4 variants)")
+    ap.add_argument("--config", default="default",
+                    help="'default': the headline decode line with every base workload "
+                         "measured in the same process under 'workloads'; or a workload "
+                         "name or index, 'all' (one line per base workload) or 'mx' (their "
+                         "MXFP4 variants)")
     ap.add_argument("--copies", type=int, default=0,
                     help="key-cache copies to rotate over (0: 4 for the decode workloads, "
                          "so that the 256 MB Infinity Cache cannot serve a step from the "
                          "one before; 1 otherwise)")
     ap.add_argument("--family", type=int, default=-1, help="-1 auto, 0 decode, 1 prefill tiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="whole output rows of a prefill workload the oracle computes for "
+                         "its CPU baseline")
     ap.add_argument("--topk", action="store_true",
                     help="time the top-k block selection on the workload's scores instead")
     ap.add_argument("--cpu-topk-rows", type=int, default=200000)
@@ -404,6 +544,20 @@ def main():
 
     import synth
     names = list(synth.CONFIG_NAMES) + list(synth.MX_CONFIG_NAMES)
+    local_mode = 1 if args.local_mode == "query" else 0
+    if args.config == "default":
+        host = host_cpu() if not args.no_cpu_baseline else None
+        recs = []
+        for c, name in enumerate(synth.CONFIG_NAMES):
+            copies = args.copies if args.copies > 0 else (4 if name.startswith("decode") else 1)
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            recs.append(bench_config(c, args.steps, args.warmup, copies, args.family,
+                                     not args.no_cpu_baseline, args, local_mode=local_mode,
+                                     topk=name.startswith("prefill"), host=host))
+        head = dict(next(r for r in recs if r["config"]["workload"] == HEADLINE))
+        head["workloads"] = [workload_summary(r) for r in recs]
+        print(json.dumps(head), flush=True)
+        return
     if args.config == "all":
         todo = list(range(len(synth.CONFIG_NAMES)))
     elif args.config == "mx":
@@ -424,8 +578,7 @@ def main():
         if copies <= 0:
             copies = 4 if names[c].startswith("decode") else 1
         r = bench_config(c, args.steps, args.warmup, copies, args.family,
-                         not args.no_cpu_baseline, args,
-                         local_mode=1 if args.local_mode == "query" else 0)
+                         not args.no_cpu_baseline, args, local_mode=local_mode)
         print(json.dumps(r), flush=True)
 
 

@@ -49,3 +49,39 @@ def test_traffic_only_for_current_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("now") == 123
     assert bench.measured_traffic("old") is None
     assert bench.measured_traffic("absent") is None
+
+
+def test_host_cpu_reports_the_share_it_uses(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    h = bench.host_cpu()
+    for k in ("nproc", "affinity", "cgroup_cpus", "omp_num_threads", "cpu_model",
+              "cores_available"):
+        assert k in h
+    assert h["omp_num_threads"] == 3
+    assert 1 <= h["cores_available"] <= min(3, h["affinity"])
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    h = bench.host_cpu()
+    assert h["omp_num_threads"] is None
+    assert h["cores_available"] <= h["affinity"] <= (h["nproc"] or h["affinity"])
+
+
+def test_cpu_baseline_legs():
+    import argparse
+    args = argparse.Namespace(cpu_rows=2)
+    host = dict(bench.host_cpu(), cores_available=2)
+    tiny = synth.config_case(0)
+    r = bench.cpu_baseline_leg(tiny, bench.workload_stats(tiny), args, host)
+    assert r["kind"] == "oracle" and r["cores"] == 2 and r["value"] > 0
+    assert r["host"]["cpu_model"] == host["cpu_model"] and not r["extrapolated"]
+    # the whole tiny example on one core too: 512 block scores
+    assert r["single_core"]["cores"] == 1 and not r["single_core"]["extrapolated"]
+    assert "512 block scores" in r["single_core"]["sample"]
+    pre = synth.config_case(2)
+    r = bench.cpu_baseline_leg(pre, bench.workload_stats(pre), args, host)
+    assert r["extrapolated"] and r["value"] > 0 and "2 whole rows" in r["sample"]
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)), ids=[c.name for c in CASES])
+def test_per_token_visible_blocks_sum_to_the_score_count(idx):
+    c = CASES[idx]
+    assert int(bench.visible_blocks_per_token(c).sum()) * c.Hq == bench.workload_stats(c)["scores"]
