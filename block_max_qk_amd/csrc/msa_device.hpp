@@ -107,6 +107,34 @@ __device__ __forceinline__ void wave_min_max(uint32_t x, uint32_t y, uint32_t& l
   hi = max(max(lane(b, 0), lane(b, 16)), max(lane(b, 32), lane(b, 48)));
 }
 
+// max(x[l], x[l ^ 32]) in every lane l: v_permlane32_swap exchanges the
+// upper half of its first register with the lower half of its second, so two
+// copies of x become the two halves side by side, and one v_max_f32 combines
+// them.  (Written out: clang's builtin for the swap loses its second result
+// in this toolchain, and a separate fmaxf on asm results adds canonicalising
+// maxima.)  The nops are the wait states around the cross-lane operation.
+__device__ __forceinline__ float max_xor32(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a);
+}
+
+// Fourth word of a raw buffer descriptor on this architecture (32-bit data
+// format; stride 0 makes the size a byte count checked per access, and
+// accesses past it read zeros).
+constexpr int kBufferWord3 = 0x00020000;
+
+// One 16-byte piece per lane from a raw buffer (byte offset voff) straight
+// into LDS: lane l's piece lands at lds + 16 l (the base goes through M0).
+// (A helper of its own: called from a lambda inside a kernel template, the
+// builtin made the host pass drop that kernel's launch stub.)
+__device__ __forceinline__ void buffer_copy16_lds(__amdgpu_buffer_rsrc_t rs, uint8_t* lds,
+                                                  uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ i32x4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }
@@ -224,6 +252,26 @@ __device__ __forceinline__ Work locate(const Params& p) {
   return w;
 }
 
+// The work item with every field in scalar registers.  locate() broadcasts
+// them from one lane with shuffles, which leaves them in vector registers;
+// values derived from them (block bases, kv_len tests) are then vector values
+// too, and branches on them run both ways under lane masks.
+__device__ __forceinline__ Work uniform_work(Work w) {
+  auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  w.valid = u(w.valid);
+  w.hk = u(w.hk);
+  w.hc = u(w.hc);
+  w.c0 = u(w.c0);
+  w.c1 = u(w.c1);
+  w.b = u(w.b);
+  w.t0 = u(w.t0);
+  w.ntok = u(w.ntok);
+  w.Lq = u(w.Lq);
+  w.L = u(w.L);
+  w.koff = uniform64(w.koff);
+  return w;
+}
+
 // Last visible key index of query token t of the work item's request:
 // min(q_pos, kv_len - 1), with q_pos = kv_len - L_q + i under the right-down
 // causal mode and kv_len - 1 without it (issue #4117, section 计算过程;
@@ -243,10 +291,13 @@ __device__ __forceinline__ int last_visible(const Params& p, const Work& w, int 
 // L - Lq + i, -1 (no window) before position 0 -- the paper's per-query local
 // block (notes "MiniMax Sparse Attention: paper algorithm and code", section
 // 4.7, forced local block).
-__device__ __forceinline__ int local_anchor(const Params& p, const Work& w, int i) {
-  if (!p.local_per_query) return p.start_loc[w.b];
+__device__ __forceinline__ int query_anchor(const Work& w, int i) {
   const int pos = w.L - w.Lq + i;
   return pos >= 0 ? pos / kP : -1;
+}
+
+__device__ __forceinline__ int local_anchor(const Params& p, const Work& w, int i) {
+  return p.local_per_query ? query_anchor(w, i) : p.start_loc[w.b];
 }
 
 __device__ __forceinline__ float finish(const Params& p, int L, int start, int beta,

@@ -548,6 +548,42 @@ void decode_kernel(Params p) {
 // prefill
 // ---------------------------------------------------------------------------
 
+// Columns [c_lo, c_hi) (multiples of 4) of every output row of a prefill
+// work item's tile where no block is scored: -inf, with the local_mask
+// constants where the init blocks or a row's local window fall (guide to
+// msa_index_score, sections 二 and 四).  Each wave takes four rows at a
+// time, sixteen lanes to a row and one 16-byte store per lane, so an
+// instruction writes whole row segments; pieces that miss both windows skip
+// the per-column rule.
+__device__ __forceinline__ void fill_tile_columns(const Params& p, const Work& w, int i0,
+                                                  int c_lo, int c_hi) {
+  const int np4 = (c_hi - c_lo) >> 2;
+  if (np4 <= 0) return;
+  const int l = lane_id();
+  const int nrows = p.hpt * w.ntok;
+  const bool marks = w.L > 0 && (p.init_blocks > 0 || p.local_blocks > 0);
+  // the request's window end, read once (per query: from each row's position)
+  const int req_anchor = (marks && !p.local_per_query) ? p.start_loc[w.b] : -1;
+  const int nwaves = blockDim.x >> 6;
+  for (int r = 4 * (threadIdx.x >> 6) + (l >> 4); r < nrows; r += 4 * nwaves) {
+    const int ti = r / p.hpt;
+    const int hg = w.hc * p.hpt + (r - ti * p.hpt);
+    if (hg >= p.g) continue;
+    float* const row = p.out + (((int64_t)w.hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W;
+    const int anchor = !marks ? -1 : p.local_per_query ? query_anchor(w, i0 + ti) : req_anchor;
+    const int lo = max(0, anchor + 1 - p.local_blocks);
+    for (int q = l & 15; q < np4; q += 16) {
+      const int beta = c_lo + 4 * q;
+      f32x4 v = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      if (marks && (beta < p.init_blocks || (beta + 3 >= lo && beta <= anchor))) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, anchor, beta + e, false, 0.f);
+      }
+      *reinterpret_cast<f32x4*>(row + beta) = v;
+    }
+  }
+}
+
 template <int KK>
 __global__ __launch_bounds__(256, (Kind<KK>::is_i8 || prefill_ntw(KK) >= 3) ? 2 : 3)
 void prefill_kernel(Params p) {
@@ -584,11 +620,13 @@ void prefill_kernel(Params p) {
   // compiler wait for every load in flight before each one)
   __shared__ int32_t kpg[Kd::is_fp4 ? kPrefillWaves : 1][CHUNK];
 
-  const Work w = locate(p);
+  const Work w = uniform_work(locate(p));
   if (!w.valid) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // a scalar, so that the LDS destinations of the key copies (which go
+  // through M0) are computed in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane_id();
   const int n = l & 31;          // row within an N tile / key token within an M tile
   const int G = l >> 5;          // k group, 0..1
@@ -599,6 +637,11 @@ void prefill_kernel(Params p) {
   const int lim_hi = (w.L > 0 && w.ntok > 0) ? last_visible(p, w, i0 + w.ntok - 1) : -1;
   const int vend = min(min(w.c1, nb), lim_hi >= 0 ? lim_hi / kP + 1 : 0);
   const bool busy = w.c0 < vend;      // some block of this work item is visible
+  if (!busy) {
+    // nothing to score: the item's columns are fill only
+    fill_tile_columns(p, w, i0, w.c0, w.c1);
+    return;
+  }
 
   int lim[NTW];
   i32x4 qv[NTW][8];
@@ -668,23 +711,34 @@ void prefill_kernel(Params p) {
   // them): token rows at or past kv_len copy row 0 of the block instead, which
   // the masked path discards
   // copy instruction q of stage sg
+  constexpr int RPI = 1024 / RB;                    // tokens per copy instruction
+  // This lane's byte offset within a stage for each of its wave's copy
+  // instructions (token jl of the stage, swizzled 16-byte chunk c), computed
+  // once per work item.
+  constexpr int NCOF = ASYNC ? NI : 1;
+  uint32_t cof[NCOF];
+#pragma unroll
+  for (int q = 0; q < NCOF; ++q) {
+    const int jl = (wave * NI + q) * RPI + l / (RB / 16);
+    const int c = (l % (RB / 16)) ^
+                  (RB == 256 ? (jl & 15) : RB == 128 ? ((jl >> 1) & 7) : ((jl >> 2) & 3));
+    cof[q] = (uint32_t)(jl * p.k_row_stride + 16 * c);
+  }
+  // Copy instruction q of stage sg, through a raw buffer over the block's
+  // rows below kv_len (its size nvalid rows): lanes of rows at or past
+  // kv_len read zeros, which only blocks that take the masked path contain.
+  // No per-copy branch or clamp; the block base and LDS destination are
+  // scalar values.
   auto stage_copy = [&](int q, int sg, int slot, int64_t kbytes) {
     const int beta = w.c0 + sg / SPB;
     const int off = (sg % SPB) * ST;
-    // wave-uniform block base; offsets within a block fit 32 bits (checked on
-    // the host)
+    // offsets within a block fit 32 bits (checked on the host)
     const uint8_t* kb = p.k + uniform64(kbytes + (int64_t)w.hk * p.k_head_stride);
     const int nvalid = min(kP, w.L - beta * kP);
-    constexpr int RPI = 1024 / RB;                  // tokens per copy instruction
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kb), 0, nvalid * p.k_row_stride, kBufferWord3);
     const int X = wave * NI + q;
-    const int jl = X * RPI + l / (RB / 16);         // token within the stage
-    const int pos = l % (RB / 16);
-    const int c = pos ^ (RB == 256 ? (jl & 15) : RB == 128 ? ((jl >> 1) & 7) : ((jl >> 2) & 3));
-    const int jj = off + jl;
-    const int src = jj < nvalid ? jj : 0;
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>(kb + (uint32_t)(src * p.k_row_stride + 16 * c)),
-        (__attribute__((address_space(3))) void*)(kl + slot * SBYTES + X * 1024), 16, 0, 0);
+    buffer_copy16_lds(rs, kl + slot * SBYTES + X * 1024, (uint32_t)(off * p.k_row_stride) + cof[q]);
   };
   // MXFP4: stage the scale words of the work item's nblk blocks into kmx
   // (rows past kv_len read row 0; their scores are masked).  Entry e = tid +
@@ -788,12 +842,21 @@ void prefill_kernel(Params p) {
   f32x4 run;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
-  // Block results of this lane's row collect in registers, RG blocks at a
-  // time, and are written as RG consecutive floats (16-byte stores).  16-bit
-  // keys run at the register limit and flush every 4 blocks; fp8 and int8
-  // once per work item.
-  constexpr int RG = (ASYNC && RB == 256) ? 4 : 16;
-  float resv[NOUT][RG];
+  // Block results of this lane's row collect RG blocks at a time and are
+  // written as RG consecutive floats (16-byte stores).  16-bit keys run at
+  // the register limit and flush every 4 blocks; MXFP4 every 8, fp8 and int8
+  // every 16.
+  // MXFP4: a block's result for each output row goes to a per-wave LDS area,
+  // one store per row, and the flush reads a row's RG values back; choosing
+  // the register of a block by its (uniform but not constant) position in the
+  // group takes a select per register and row, 32 VALU instructions per block
+  // against 32 MFMAs.  Groups of 8 blocks keep two workgroups within a CU's
+  // LDS.  (For fp8 the extra LDS array made the compiler wait for the next
+  // stage's copies before fragment reads in the block loop.)
+  constexpr bool LDS_RES = Kd::is_fp4;
+  constexpr int RG = (ASYNC && RB == 256) ? 4 : Kd::is_fp4 ? 8 : 16;
+  __shared__ float resl[LDS_RES ? kPrefillWaves : 1][LDS_RES ? NOUT : 1][LDS_RES ? RG : 1][64];
+  float resv[NOUT][LDS_RES ? 1 : RG];
   int pend = -1;                 // first block of a group waiting to be written
   auto flush = [&](int g0) {
 #pragma unroll
@@ -806,7 +869,12 @@ void prefill_kernel(Params p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int beta = g0 + c + e;
-              v[e] = finish(p, w.L, oanc[u], beta, beta < vend, resv[u][c + e]);
+              float r;
+              if constexpr (LDS_RES)
+                r = resl[wave][u][c + e][l];
+              else
+                r = resv[u][c + e];
+              v[e] = finish(p, w.L, oanc[u], beta, beta < vend, r);
             }
             *reinterpret_cast<f32x4*>(orow_ptr[u] + g0 + c) = v;
           }
@@ -966,13 +1034,17 @@ void prefill_kernel(Params p) {
     if (off + ST == kP) {
       // the two k groups hold the two halves of each 32-token M tile
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) run[nt] = fmaxf(run[nt], __shfl_xor(run[nt], 32, 64));
+      for (int nt = 0; nt < NTW; ++nt) run[nt] = max_xor32(run[nt]);
       const int kk = (beta - w.c0) % RG;
 #pragma unroll
       for (int u = 0; u < NOUT; ++u) {
         const float v = (G && 2 * u + 1 < NTW) ? run[2 * u + 1] : run[2 * u];
+        if constexpr (LDS_RES) {
+          resl[wave][u][kk][l] = v;
+        } else {
 #pragma unroll
-        for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+          for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+        }
       }
       if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
     }
@@ -983,18 +1055,7 @@ void prefill_kernel(Params p) {
 
   if (pend >= 0) flush(pend);
   // columns of the work item past the last group: -inf and local_mask
-  const int done = busy ? w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG : w.c0;
-#pragma unroll
-  for (int u = 0; u < NOUT; ++u) {
-    if (orow_ok[u]) {
-      for (int beta = done; beta < w.c1; beta += 4) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, oanc[u], beta + e, false, 0.f);
-        *reinterpret_cast<f32x4*>(orow_ptr[u] + beta) = v;
-      }
-    }
-  }
+  fill_tile_columns(p, w, i0, w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG, w.c1);
 }
 
 }  // namespace msa

@@ -40,9 +40,6 @@ __device__ __forceinline__ uint32_t topk_key(float f) {
 __device__ __forceinline__ uint32_t below_mask(int b, int n) { return (uint32_t)((b - n) >> 31); }
 
 constexpr int kTopkWaves = 4;  // waves per workgroup
-// Fourth word of a raw buffer descriptor on this architecture (32-bit data
-// format; stride 0 makes the size a byte count checked per access).
-constexpr int kBufferWord3 = 0x00020000;
 // Cache-policy operand of a buffer access: the nontemporal bit.
 constexpr int kCachePolicyNT = 2;
 // From this many rows on, each wave takes two rows in turn.
