@@ -28,6 +28,9 @@
 namespace msa {
 
 constexpr int kTopkMax = 64;   // k is at most one wave of lanes
+// A wave's LDS area holds 128 entries: 64 compacted ones, then a spare entry
+// per lane for the stores of lanes with nothing to compact.
+constexpr int kTopkSpare = 64;
 
 // Order-preserving key of a score that can be selected; 0 for -inf and NaN.
 __device__ __forceinline__ uint32_t topk_key(float f) {
@@ -45,23 +48,18 @@ constexpr int kCachePolicyNT = 2;
 // From this many rows on, each wave takes two rows in turn.
 constexpr int64_t kTopkManyRows = 65536;
 
-// The selection on one row whose scores (J > 0) are already in v: v[j] in
-// lane l holds block 64 j + l (any value past nv).  J = 0 re-reads the row.
+// The threshold search on one row.  J > 0: keys[j] in lane l is the key
+// (topk_key, 0 past nv) of block 64 j + l.  J = 0 re-reads the row.
 // slot: this wave's 128-entry LDS area; sel: its 64-entry output area.  The
 // k results go to dst with one store per lane (lanes past k repeat slot k - 1),
 // so every row issues the same memory operations.
 template <int J>
-__device__ __forceinline__ void topk_row(const float* __restrict__ row, const float (&v)[J > 0 ? J : 1],
-                                         int nv, int k, int32_t* __restrict__ dst, uint2* slot,
-                                         int32_t* sel) {
+__device__ __forceinline__ void topk_row_search(const float* __restrict__ row,
+                                                const uint32_t (&keys)[J > 0 ? J : 1], int nv, int k,
+                                                int32_t* __restrict__ dst, uint2* slot, int32_t* sel) {
   const int l = lane_id();
   const int nch = (nv + 63) / 64;          // 64-block chunks holding candidates
   const int nj = J > 0 ? J : nch;
-  uint32_t keys[J > 0 ? J : 1];
-  if constexpr (J > 0) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) keys[j] = topk_key(v[j]) & below_mask(j * 64 + l, nv);
-  }
   auto key = [&](int j) -> uint32_t {
     if constexpr (J > 0) {
       return keys[j];
@@ -234,6 +232,183 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, const fl
   wave_lds_sync();
   const int o = min(l, k - 1);
   dst[o] = sel[o];
+}
+
+// Rotated key: topk_key's order on every selectable score, moved up by
+// 2^23 - 1 with wrap-around, so that NaN and -inf fall below kKeyFloor (the
+// key of -FLT_MAX) and no compare or select is needed to exclude them.
+constexpr uint32_t kKeyShift = 0x007FFFFFu;
+constexpr uint32_t kKeyFloor = 0x00FFFFFFu;
+__device__ __forceinline__ uint32_t topk_key_rot(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) + kKeyShift;
+}
+
+// The fast path covers k up to this many.
+constexpr int kTopkFastK = 16;
+
+// Selection on one row held in registers, for k <= 16: rk[j] in lane l is the
+// rotated key of block 64 j + l (0 past nv).  Returns false, having written
+// nothing to dst, when more than 64 keys reach the lower bound below; the
+// caller then runs the general search.
+//
+// Lower bound: in each eight-lane half row, the two largest lane maxima are
+// keys of two different blocks, so the smallest such second maximum over the
+// eight half rows, t0, is reached by at least 16 >= k keys: the k-th largest
+// key is >= t0.  On rows of independent scores about 30 keys reach t0, so
+// one pass compacts them (in index order) into one register per lane, and
+// the threshold search runs on that register alone: no step of it reads the
+// whole row again.
+template <int J>
+__device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
+                                              int32_t* __restrict__ dst, uint2* slot,
+                                              int32_t* sel) {
+  const int l = lane_id();
+  uint32_t m = rk[0];
+#pragma unroll
+  for (int j = 1; j < J; ++j) m = max(m, rk[j]);
+  // the two largest lane maxima (a1 >= a2) of every pair, quad, then half row
+  uint32_t a1, a2;
+  {
+    const uint32_t b = dpp_u32<0xB1>(m);  // quad_perm 1,0,3,2
+    a1 = max(m, b);
+    a2 = min(m, b);
+  }
+  {
+    const uint32_t b1 = dpp_u32<0x4E>(a1), b2 = dpp_u32<0x4E>(a2);  // quad_perm 2,3,0,1
+    a2 = max(min(a1, b1), max(a2, b2));
+    a1 = max(a1, b1);
+  }
+  {
+    const uint32_t b1 = dpp_u32<0x141>(a1), b2 = dpp_u32<0x141>(a2);  // row_half_mirror
+    a2 = max(min(a1, b1), max(a2, b2));
+  }
+  a2 = min(a2, dpp_u32<0x140>(a2));  // row_mirror: both half rows of a row
+  auto lane = [](uint32_t x, int i) { return (uint32_t)__builtin_amdgcn_readlane((int)x, i); };
+  const uint32_t t0 = max(min(min(lane(a2, 0), lane(a2, 16)), min(lane(a2, 32), lane(a2, 48))),
+                          kKeyFloor);
+
+  // compaction of the keys >= t0, in index order, as (key, block) entries.
+  // Each store goes to the area's byte address 8 min(base, 64) (scalar) plus
+  // 8 times the lane's rank in the chunk; lanes whose key does not qualify
+  // write to their spare entry, so the stores need no branch.  A row with
+  // more than 64 such keys goes to the general search; until this pass ends
+  // its stores stay inside the area (index at most 64 + 63).
+  // (The lane number passes through an empty asm so that the block numbers
+  // are formed at each store rather than held in registers across rows.)
+  uint32_t lv = (uint32_t)l;
+  asm volatile("" : "+v"(lv));
+  char* const area = reinterpret_cast<char*>(slot);
+  uint2* const spare = slot + kTopkSpare + l;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const bool q = rk[j] >= t0;
+    const uint64_t mk = __ballot(q);
+    const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    uint2* const at = reinterpret_cast<uint2*>(area + 8 * min(base, 64)) + r;
+    *(q ? at : spare) = make_uint2(rk[j], lv + (uint32_t)(j * 64));
+    base += __popcll(mk);
+  }
+  if (base > 64) return false;
+  wave_lds_sync();
+  const uint2 e = slot[l];
+  const uint32_t ck = l < base ? e.x : 0u;   // 0: no candidate in this lane
+
+  // tau: the k-th largest compacted key, or a lower threshold that exactly k
+  // keys reach; below every candidate when there are at most k.
+  uint32_t tau = kKeyFloor - 1u;
+  if (base > k) {
+    // Bounds: t0 from below.  From above, the largest compacted key under
+    // the key of 1e28 when fewer than k keys reach that key (the forced
+    // local_mask values 1e30 and 1e29 are the only scores that do, far above
+    // every computed one), else the largest key.
+    const uint32_t hi_cut = topk_key_rot(1e28f);
+    const int n_hi = __popcll(__ballot(ck >= hi_cut));
+    uint32_t x = (n_hi < k && ck >= hi_cut) ? 0u : ck;
+    x = max(x, dpp_u32<0xB1>(x));
+    x = max(x, dpp_u32<0x4E>(x));
+    x = max(x, dpp_u32<0x141>(x));
+    x = max(x, dpp_u32<0x140>(x));
+    const uint32_t ub = __builtin_amdgcn_readfirstlane(
+        max(max(lane(x, 0), lane(x, 16)), max(lane(x, 32), lane(x, 48))));
+    // tau takes the leading bits t0 and ub share; the search goes on below
+    // them, one bit a step: the bit stays when at least k keys reach
+    // tau | bit, and the search ends once exactly k do (scalar registers
+    // throughout, one vector compare a step)
+    if (t0 >= ub) {
+      tau = ub;
+    } else {
+      uint32_t mb = 0x80000000u >> __builtin_clz(t0 ^ ub);
+      tau = ub & ~(2u * mb - 1u);
+      uint32_t c, n;
+      asm volatile(
+          "1:\n\t"
+          "s_or_b32 %[c], %[tau], %[mb]\n\t"
+          "v_cmp_le_u32 vcc, %[c], %[ck]\n\t"
+          "s_bcnt1_i32_b64 %[n], vcc\n\t"
+          "s_cmp_ge_u32 %[n], %[k]\n\t"
+          "s_cselect_b32 %[tau], %[c], %[tau]\n\t"
+          "s_cmp_eq_u32 %[n], %[k]\n\t"
+          "s_cbranch_scc1 2f\n\t"
+          "s_lshr_b32 %[mb], %[mb], 1\n\t"
+          "s_cmp_lg_u32 %[mb], 0\n\t"
+          "s_cbranch_scc1 1b\n"
+          "2:"
+          : [tau] "+s"(tau), [mb] "+s"(mb), [c] "=&s"(c), [n] "=&s"(n)
+          : [ck] "v"(ck), [k] "s"((uint32_t)k)
+          : "vcc", "scc");
+    }
+  }
+  // keys above tau all fit; ties at tau fill the remaining slots, lowest
+  // index first; the taken blocks, in index order, then -1
+  auto rank_in = [](uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+  };
+  const int need_eq = k - __popcll(__ballot(ck > tau));
+  const bool eq = ck == tau;
+  const bool take = ck > tau || (eq && rank_in(__ballot(eq)) < need_eq);
+  const uint64_t tm = __ballot(take);
+  if (take) sel[rank_in(tm)] = (int32_t)e.y;
+  const int taken = __popcll(tm);
+  wave_lds_sync();
+  const int o = min(l, k - 1);
+  const int32_t got = sel[o];
+  dst[o] = o < taken ? got : -1;
+  return true;
+}
+
+// The selection on one row whose scores (J > 0) are already in v: v[j] in
+// lane l holds block 64 j + l (any value past nv).  J = 0 re-reads the row.
+template <int J>
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, const float (&v)[J > 0 ? J : 1],
+                                         int nv, int k, int32_t* __restrict__ dst, uint2* slot,
+                                         int32_t* sel) {
+  uint32_t keys[J > 0 ? J : 1];
+  if constexpr (J > 0) {
+    const int l = lane_id();
+    if (nv == 64 * J) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) keys[j] = topk_key_rot(v[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) keys[j] = j * 64 + l < nv ? topk_key_rot(v[j]) : 0u;
+    }
+    if (k <= kTopkFastK && topk_row_fast<J>(keys, k, dst, slot, sel)) return;
+    // the general search, on the row read again (from L2, rarely): the fast
+    // path's registers are then free for it
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row), 0, 4 * nv, kBufferWord3);
+    uint32_t lv = (uint32_t)l;             // formed here, not held from the kernel's start
+    asm volatile("" : "+v"(lv));
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      keys[j] = topk_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lv + 256 * j, 0, 0))) &
+                below_mask(j * 64 + (int)lv, nv);
+  }
+  topk_row_search<J>(row, keys, nv, k, dst, slot, sel);
 }
 
 // grid (ceil(T / (4 R)), Hq): wave w of block (x, h) takes the rows
