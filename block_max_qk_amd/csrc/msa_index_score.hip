@@ -400,19 +400,19 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nv = (int)num_valid;
   // Keys of up to 64 * J blocks stay in registers, longer rows are re-read.
-  // With many rows a wave takes R = 2 of them in turn (the second row's
-  // loads overlap the selection on the first); few rows keep one per wave,
-  // for parallelism.
-  const bool many = Hq * T >= (int64_t)msa::kTopkManyRows && nv <= 2048;
-  const int R = many ? 2 : 1;
+  // With many rows of up to 512 blocks a wave takes R = 4 of them in turn
+  // (each row's loads overlap the selection on the row before); few rows
+  // keep one per wave, for parallelism, and so do longer rows, where a
+  // second row's registers would cost occupancy.
+  const int R = Hq * T >= (int64_t)msa::kTopkManyRows && nv <= 512 ? 4 : 1;
   const dim3 grid((unsigned)((T + msa::kTopkWaves * R - 1) / (msa::kTopkWaves * R)), (unsigned)Hq);
   const dim3 block(64 * msa::kTopkWaves);
   hipError_t e;
 #define MSA_TOPK_LAUNCH(J)                                                                        \
-  e = many ? launch_kernel(msa::topk_kernel<J, 2>, grid, block, s, scores, T, Hq, width, nv, k,   \
-                           out)                                                                   \
-           : launch_kernel(msa::topk_kernel<J, 1>, grid, block, s, scores, T, Hq, width, nv, k,   \
-                           out)
+  e = R == 4 ? launch_kernel(msa::topk_kernel<J, 4>, grid, block, s, scores, T, Hq, width, nv, k,   \
+                             out)                                                                 \
+             : launch_kernel(msa::topk_kernel<J, 1>, grid, block, s, scores, T, Hq, width, nv, k,   \
+                             out)
   if (nv <= 128)
     MSA_TOPK_LAUNCH(2);
   else if (nv <= 256)
@@ -420,9 +420,9 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   else if (nv <= 512)
     MSA_TOPK_LAUNCH(8);
   else if (nv <= 1024)
-    MSA_TOPK_LAUNCH(16);
+    e = launch_kernel(msa::topk_kernel<16, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
   else if (nv <= 2048)
-    MSA_TOPK_LAUNCH(32);
+    e = launch_kernel(msa::topk_kernel<32, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
   else
     e = launch_kernel(msa::topk_kernel<0, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
 #undef MSA_TOPK_LAUNCH

@@ -247,6 +247,28 @@ __device__ __forceinline__ uint32_t topk_key_rot(float f) {
 // The fast path covers k up to this many.
 constexpr int kTopkFastK = 16;
 
+// x holds, in every lane of each row of 16 lanes, that row's value; the
+// smallest (or largest) over the four rows: row_bcast:15 passes lane 15 of
+// each row to the next row (rows 1 and 3 take it), row_bcast:31 lane 31 to
+// rows 2 and 3, so lane 63 ends with all four.
+// (Written out: one DPP min or max per step, the rows outside the row mask
+// keeping their value; the nops are the wait states a DPP read needs after a
+// vector write of its source.)
+template <bool MAX>
+__device__ __forceinline__ uint32_t rows_combine(uint32_t x) {
+  if constexpr (MAX)
+    asm volatile(
+        "s_nop 1\n\tv_max_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\ts_nop 1"
+        : "+v"(x));
+  else
+    asm volatile(
+        "s_nop 1\n\tv_min_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_min_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\ts_nop 1"
+        : "+v"(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Selection on one row held in registers, for k <= 16: rk[j] in lane l is the
 // rotated key of block 64 j + l (0 past nv).  Returns false, having written
 // nothing to dst, when more than 64 keys reach the lower bound below; the
@@ -284,9 +306,7 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
     a2 = max(min(a1, b1), max(a2, b2));
   }
   a2 = min(a2, dpp_u32<0x140>(a2));  // row_mirror: both half rows of a row
-  auto lane = [](uint32_t x, int i) { return (uint32_t)__builtin_amdgcn_readlane((int)x, i); };
-  const uint32_t t0 = max(min(min(lane(a2, 0), lane(a2, 16)), min(lane(a2, 32), lane(a2, 48))),
-                          kKeyFloor);
+  const uint32_t t0 = max(rows_combine<false>(a2), kKeyFloor);
 
   // compaction of the keys >= t0, in index order, as (key, block) entries.
   // Each store goes to the area's byte address 8 min(base, 64) (scalar) plus
@@ -294,10 +314,11 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
   // write to their spare entry, so the stores need no branch.  A row with
   // more than 64 such keys goes to the general search; until this pass ends
   // its stores stay inside the area (index at most 64 + 63).
-  // (The lane number passes through an empty asm so that the block numbers
-  // are formed at each store rather than held in registers across rows.)
+  // (For J > 8 the lane number passes through an empty asm, so that the
+  // block numbers are formed at each store rather than held in registers
+  // across rows.)
   uint32_t lv = (uint32_t)l;
-  asm volatile("" : "+v"(lv));
+  if constexpr (J > 8) asm volatile("" : "+v"(lv));
   char* const area = reinterpret_cast<char*>(slot);
   uint2* const spare = slot + kTopkSpare + l;
   int base = 0;
@@ -331,8 +352,7 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
     x = max(x, dpp_u32<0x4E>(x));
     x = max(x, dpp_u32<0x141>(x));
     x = max(x, dpp_u32<0x140>(x));
-    const uint32_t ub = __builtin_amdgcn_readfirstlane(
-        max(max(lane(x, 0), lane(x, 16)), max(lane(x, 32), lane(x, 48))));
+    const uint32_t ub = rows_combine<true>(x);
     // tau takes the leading bits t0 and ub share; the search goes on below
     // them, one bit a step: the bit stays when at least k keys reach
     // tau | bit, and the search ends once exactly k do (scalar registers
@@ -352,8 +372,7 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
           "s_cselect_b32 %[tau], %[c], %[tau]\n\t"
           "s_cmp_eq_u32 %[n], %[k]\n\t"
           "s_cbranch_scc1 2f\n\t"
-          "s_lshr_b32 %[mb], %[mb], 1\n\t"
-          "s_cmp_lg_u32 %[mb], 0\n\t"
+          "s_lshr_b32 %[mb], %[mb], 1\n\t"   // SCC: the result is not 0
           "s_cbranch_scc1 1b\n"
           "2:"
           : [tau] "+s"(tau), [mb] "+s"(mb), [c] "=&s"(c), [n] "=&s"(n)
@@ -367,10 +386,14 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
   };
-  const int need_eq = k - __popcll(__ballot(ck > tau));
-  const bool eq = ck == tau;
-  const bool take = ck > tau || (eq && rank_in(__ballot(eq)) < need_eq);
-  const uint64_t tm = __ballot(take);
+  bool take = ck >= tau;
+  uint64_t tm = __ballot(take);
+  if (__popcll(tm) > k) {                  // ties at tau (rare)
+    const int need_eq = k - __popcll(__ballot(ck > tau));
+    const bool eq = ck == tau;
+    take = ck > tau || (eq && rank_in(__ballot(eq)) < need_eq);
+    tm = __ballot(take);
+  }
   if (take) sel[rank_in(tm)] = (int32_t)e.y;
   const int taken = __popcll(tm);
   wave_lds_sync();

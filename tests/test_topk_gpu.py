@@ -86,6 +86,41 @@ def test_degenerate_rows(dev):
     assert gpu_topk(s, dev, 0, 16).eq(-1).all()
 
 
+def limit_rows(W):
+    """Rows at the limits of the register path's compaction (64 entries) and
+    of its upper bound (forced local_mask blocks around k)."""
+    g = torch.Generator().manual_seed(77 + W)
+    rows = []
+    for n in (16, 17, 63, 64, 65, 128):        # n equal candidates, -inf elsewhere
+        r = torch.full((W,), float("-inf"))
+        r[:n] = 1.0
+        rows.append(r)
+    for n in (64, 65):                          # n distinct candidates spread over the row
+        r = torch.full((W,), float("-inf"))
+        r[torch.randperm(W, generator=g)[:n]] = torch.randn(n, generator=g) * 11 + 30
+        rows.append(r)
+    for f in (15, 16, 17, 40):                  # f forced blocks on computed scores
+        r = torch.randn(W, generator=g) * 11 + 30
+        pos = torch.randperm(W, generator=g)[:f]
+        r[pos] = 1e29
+        r[pos[: f // 3]] = 1e30
+        rows.append(r)
+    r = torch.randn(W, generator=g) * 11 + 30   # NaN and -inf holes among the scores
+    r[torch.randperm(W, generator=g)[: W // 4]] = float("nan")
+    r[torch.randperm(W, generator=g)[: W // 4]] = float("-inf")
+    rows.append(r)
+    return torch.stack(rows)[None].contiguous()
+
+
+@pytest.mark.parametrize("W", [512, 1024])
+def test_compaction_and_bound_limits(W, dev):
+    s = limit_rows(W)
+    for nv in (W, W - 37):
+        for k in (1, 8, 16, 17):
+            log(f"topk limit rows W={W} num_valid={nv} k={k}")
+            assert torch.equal(gpu_topk(s, dev, nv, k), oracle.block_topk(s, nv, k)), (W, nv, k)
+
+
 def test_empty_sizes_launch_nothing(dev):
     import block_max_qk_amd as m
     for shape in ((0, 4, 16), (3, 0, 16)):
