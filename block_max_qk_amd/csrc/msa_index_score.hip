@@ -385,6 +385,9 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
              local_blocks, local_mode, out, out_width, stream, family, false);
 }
 
+#ifndef MSA_TOPK_R4_FULL16
+#define MSA_TOPK_R4_FULL16 0
+#endif
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
                             int64_t num_valid, int32_t k, int32_t* out, void* stream) {
   if (Hq < 0 || T < 0 || width < 0 || width > (1 << 24) || num_valid < 0 || num_valid > width)
@@ -404,28 +407,46 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   // (each row's loads overlap the selection on the row before); few rows
   // keep one per wave, for parallelism, and so do longer rows, where a
   // second row's registers would cost occupancy.
-  const int R = Hq * T >= (int64_t)msa::kTopkManyRows && nv <= 512 ? 4 : 1;
+  const int R = Hq * T >= (int64_t)msa::kTopkManyRows && (nv <= 512 || nv == MSA_TOPK_R4_FULL16) ? 4 : 1;
   const dim3 grid((unsigned)((T + msa::kTopkWaves * R - 1) / (msa::kTopkWaves * R)), (unsigned)Hq);
   const dim3 block(64 * msa::kTopkWaves);
   hipError_t e;
-#define MSA_TOPK_LAUNCH(J)                                                                        \
-  e = R == 4 ? launch_kernel(msa::topk_kernel<J, 4>, grid, block, s, scores, T, Hq, width, nv, k,   \
-                             out)                                                                 \
-             : launch_kernel(msa::topk_kernel<J, 1>, grid, block, s, scores, T, Hq, width, nv, k,   \
-                             out)
-  if (nv <= 128)
+  // (a kernel per register count J, rows per wave R, and whether nv fills
+  // the J registers exactly)
+#define MSA_TOPK_GO(J, R, F) \
+  e = launch_kernel(msa::topk_kernel<J, R, F>, grid, block, s, scores, T, Hq, width, nv, k, out)
+#define MSA_TOPK_LAUNCH(J)        \
+  if (R == 4 && nv == 64 * J)     \
+    MSA_TOPK_GO(J, 4, true);      \
+  else if (R == 4)                \
+    MSA_TOPK_GO(J, 4, false);     \
+  else if (nv == 64 * J)          \
+    MSA_TOPK_GO(J, 1, true);      \
+  else                            \
+    MSA_TOPK_GO(J, 1, false)
+  if (nv <= 128) {
     MSA_TOPK_LAUNCH(2);
-  else if (nv <= 256)
+  } else if (nv <= 256) {
     MSA_TOPK_LAUNCH(4);
-  else if (nv <= 512)
+  } else if (nv <= 512) {
     MSA_TOPK_LAUNCH(8);
-  else if (nv <= 1024)
-    e = launch_kernel(msa::topk_kernel<16, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
-  else if (nv <= 2048)
-    e = launch_kernel(msa::topk_kernel<32, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
-  else
-    e = launch_kernel(msa::topk_kernel<0, 1>, grid, block, s, scores, T, Hq, width, nv, k, out);
+  } else if (nv <= 1024) {
+    if (nv == 1024 && R == 4)
+      MSA_TOPK_GO(16, 4, true);
+    else if (nv == 1024)
+      MSA_TOPK_GO(16, 1, true);
+    else
+      MSA_TOPK_GO(16, 1, false);
+  } else if (nv <= 2048) {
+    if (nv == 2048)
+      MSA_TOPK_GO(32, 1, true);
+    else
+      MSA_TOPK_GO(32, 1, false);
+  } else {
+    MSA_TOPK_GO(0, 1, false);
+  }
 #undef MSA_TOPK_LAUNCH
+#undef MSA_TOPK_GO
   return e == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 

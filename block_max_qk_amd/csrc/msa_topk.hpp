@@ -34,7 +34,7 @@ constexpr int kTopkSpare = 64;
 
 // Order-preserving key of a score that can be selected; 0 for -inf and NaN.
 __device__ __forceinline__ uint32_t topk_key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  const uint32_t u = __float_as_uint(f + 0.0f);   // -0 and +0 are one score
   const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return f > -__builtin_inff() ? key : 0u;
 }
@@ -240,8 +240,21 @@ __device__ __forceinline__ void topk_row_search(const float* __restrict__ row,
 constexpr uint32_t kKeyShift = 0x007FFFFFu;
 constexpr uint32_t kKeyFloor = 0x00FFFFFFu;
 __device__ __forceinline__ uint32_t topk_key_rot(float f) {
-  const uint32_t u = __float_as_uint(f);
+  const uint32_t u = __float_as_uint(f + 0.0f);   // -0 and +0 are one score
   return (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) + kKeyShift;
+}
+// The score whose rotated key is r (r >= kKeyFloor).
+__device__ __forceinline__ float topk_key_rot_score(uint32_t r) {
+  const uint32_t u = r - kKeyShift;
+  return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
+// max(a, b, c) as the hardware computes it, without the quieting maxima the
+// compiler puts around fmaxf on values of unknown origin: a NaN input can
+// only lower a lane's maximum to a NaN, which the caller counts as nothing.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
 }
 
 // The fast path covers k up to this many.
@@ -269,10 +282,12 @@ __device__ __forceinline__ uint32_t rows_combine(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-// Selection on one row held in registers, for k <= 16: rk[j] in lane l is the
-// rotated key of block 64 j + l (0 past nv).  Returns false, having written
-// nothing to dst, when more than 64 keys reach the lower bound below; the
-// caller then runs the general search.
+// Selection on one row held in registers, for k <= 16: x[j] in lane l is the
+// score of block 64 j + l (-inf past nv).  Returns false, having written
+// nothing to dst, when more than 64 scores reach the lower bound below; the
+// caller then runs the general search.  Scores are compared as floats (NaN
+// and -inf never qualify) until the compaction; the compacted candidates then
+// turn into rotated keys.
 //
 // Lower bound: in each eight-lane half row, the two largest lane maxima are
 // keys of two different blocks, so the smallest such second maximum over the
@@ -282,13 +297,20 @@ __device__ __forceinline__ uint32_t rows_combine(uint32_t x) {
 // the threshold search runs on that register alone: no step of it reads the
 // whole row again.
 template <int J>
-__device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
+__device__ __forceinline__ bool topk_row_fast(const float (&x)[J], int k,
                                               int32_t* __restrict__ dst, uint2* slot,
                                               int32_t* sel) {
   const int l = lane_id();
-  uint32_t m = rk[0];
+  // the lane's largest score, as a rotated key (below kKeyFloor when the lane
+  // has nothing selectable)
+  float mf = x[0];
+  {
+    int j = 1;
 #pragma unroll
-  for (int j = 1; j < J; ++j) m = max(m, rk[j]);
+    for (; j + 1 < J; j += 2) mf = max3_raw(mf, x[j], x[j + 1]);
+    if (j < J) mf = max3_raw(mf, x[j], x[j]);
+  }
+  const uint32_t m = topk_key_rot(mf == mf ? mf : -__builtin_inff());
   // the two largest lane maxima (a1 >= a2) of every pair, quad, then half row
   uint32_t a1, a2;
   {
@@ -307,6 +329,7 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
   }
   a2 = min(a2, dpp_u32<0x140>(a2));  // row_mirror: both half rows of a row
   const uint32_t t0 = max(rows_combine<false>(a2), kKeyFloor);
+  const float t0f = topk_key_rot_score(t0);
 
   // compaction of the keys >= t0, in index order, as (key, block) entries.
   // Each store goes to the area's byte address 8 min(base, 64) (scalar) plus
@@ -320,22 +343,24 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
   uint32_t lv = (uint32_t)l;
   if constexpr (J > 8) asm volatile("" : "+v"(lv));
   char* const area = reinterpret_cast<char*>(slot);
+  char* const area_end = area + 8 * 64;
   uint2* const spare = slot + kTopkSpare + l;
-  int base = 0;
+  char* next = area;                         // area + 8 (entries so far)
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const bool q = rk[j] >= t0;
+    const bool q = x[j] >= t0f;
     const uint64_t mk = __ballot(q);
     const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    uint2* const at = reinterpret_cast<uint2*>(area + 8 * min(base, 64)) + r;
-    *(q ? at : spare) = make_uint2(rk[j], lv + (uint32_t)(j * 64));
-    base += __popcll(mk);
+    uint2* const at = reinterpret_cast<uint2*>(next < area_end ? next : area_end) + r;
+    *(q ? at : spare) = make_uint2(__float_as_uint(x[j]), lv + (uint32_t)(j * 64));
+    next += 8 * __popcll(mk);
   }
+  const int base = (int)((next - area) >> 3);
   if (base > 64) return false;
   wave_lds_sync();
   const uint2 e = slot[l];
-  const uint32_t ck = l < base ? e.x : 0u;   // 0: no candidate in this lane
+  const uint32_t ck = l < base ? topk_key_rot(__uint_as_float(e.x)) : 0u;   // 0: no candidate
 
   // tau: the k-th largest compacted key, or a lower threshold that exactly k
   // keys reach; below every candidate when there are at most k.
@@ -405,21 +430,21 @@ __device__ __forceinline__ bool topk_row_fast(const uint32_t (&rk)[J], int k,
 
 // The selection on one row whose scores (J > 0) are already in v: v[j] in
 // lane l holds block 64 j + l (any value past nv).  J = 0 re-reads the row.
-template <int J>
-__device__ __forceinline__ void topk_row(const float* __restrict__ row, const float (&v)[J > 0 ? J : 1],
+// FULL: nv == 64 J (no block past nv in the registers).
+template <int J, bool FULL>
+__device__ __forceinline__ void topk_row(const float* __restrict__ row, float (&v)[J > 0 ? J : 1],
                                          int nv, int k, int32_t* __restrict__ dst, uint2* slot,
                                          int32_t* sel) {
   uint32_t keys[J > 0 ? J : 1];
   if constexpr (J > 0) {
     const int l = lane_id();
-    if (nv == 64 * J) {
+    if (k <= kTopkFastK) {
+      if constexpr (!FULL) {
 #pragma unroll
-      for (int j = 0; j < J; ++j) keys[j] = topk_key_rot(v[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < J; ++j) keys[j] = j * 64 + l < nv ? topk_key_rot(v[j]) : 0u;
+        for (int j = 0; j < J; ++j) v[j] = j * 64 + l < nv ? v[j] : -__builtin_inff();
+      }
+      if (topk_row_fast<J>(v, k, dst, slot, sel)) return;
     }
-    if (k <= kTopkFastK && topk_row_fast<J>(keys, k, dst, slot, sel)) return;
     // the general search, on the row read again (from L2, rarely): the fast
     // path's registers are then free for it
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -438,7 +463,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ row, const fl
 // (h, t) for t = (4 x + w) R + i, i < R; rows past T repeat row T - 1 (same
 // result, same place).  Every lane loads and masks afterwards, so no load
 // carries a branch and a row's loads are all in flight together.
-template <int J, int R>
+template <int J, int R, bool FULL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, int64_t T,
                                                    int64_t Hq, int64_t W, int nv, int k,
                                                    int32_t* __restrict__ out) {
@@ -447,7 +472,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   const int64_t t0 = ((int64_t)blockIdx.x * kTopkWaves + w) * R;
   if (t0 >= T) return;
   const int64_t h = blockIdx.y;
-  auto dst_of = [&](int i) { return out + (min(t0 + i, T - 1) * Hq + h) * k; };
+  // row i of this wave is row min(i, last) (rows past T repeat row T - 1);
+  // from the wave's first row the row pointer steps by W floats and the
+  // output by Hq k entries
+  const int last = (int)min(T - 1 - t0, (int64_t)(R - 1));
+  int32_t* const out0 = out + (t0 * Hq + h) * k;
+  const int out_step = (int)Hq * k;
+  auto dst_of = [&](int i) { return out0 + min(i, last) * out_step; };
   if (nv == 0) {                           // nothing to select; scores may be NULL
     for (int i = 0; i < R; ++i)
       if (l < k) dst_of(i)[l] = -1;
@@ -455,7 +486,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   }
   __shared__ uint2 packed[kTopkWaves][128];
   __shared__ int32_t chosen[kTopkWaves][64];
-  auto row_of = [&](int i) { return scores + (h * T + min(t0 + i, T - 1)) * W; };
+  const float* const row0 = scores + (h * T + t0) * W;
+  auto row_of = [&](int i) { return row0 + min(i, last) * (int)W; };
   // A row is read through a buffer descriptor (scalar base = the row, size =
   // nv floats): lane l's load j takes byte offset 4 l + 256 j, the same for
   // every row, and offsets past the size read as 0 (masked to key 0 later).
@@ -480,7 +512,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 #pragma unroll
     for (int j = 0; j < (J > 0 ? J : 1); ++j) v[j] = vn[j];
     if (i + 1 < R) load(vn, row_of(i + 1));
-    topk_row<J>(row_of(i), v, nv, k, dst_of(i), packed[w], chosen[w]);
+    topk_row<J, FULL>(row_of(i), v, nv, k, dst_of(i), packed[w], chosen[w]);
   }
 }
 

@@ -105,6 +105,9 @@ def limit_rows(W):
         r[pos] = 1e29
         r[pos[: f // 3]] = 1e30
         rows.append(r)
+    r = torch.zeros(W)                          # -0.0 and +0.0 are one score: lower blocks first
+    r[torch.randperm(W, generator=g)[: W // 2]] = -0.0
+    rows.append(r)
     r = torch.randn(W, generator=g) * 11 + 30   # NaN and -inf holes among the scores
     r[torch.randperm(W, generator=g)[: W // 4]] = float("nan")
     r[torch.randperm(W, generator=g)[: W // 4]] = float("-inf")
