@@ -478,6 +478,94 @@ def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) ->
 HEADLINE = "decode_bbnd_bf16"
 
 
+def decode_batch_stats(kv, Hq: int, Hkv: int, D: int, P: int, MB: int, esz: int) -> dict:
+    """workload_stats for one-token decode requests (q_len = 1, right-down
+    causal window, every kv_len >= 1 and <= MB P): each request scores its
+    ceil(kv_len / P) blocks and reads its kv_len keys once."""
+    import numpy as np
+    kv = np.asarray(kv, dtype=np.int64)
+    B = int(kv.size)
+    nb = (kv - 1) // P + 1
+    W = ((max(MB, 1) + 15) // 16) * 16
+    k_bytes = int(kv.sum()) * Hkv * D * esz
+    q_bytes = B * Hq * D * 2
+    out_bytes = Hq * B * W * 4
+    return {"scores": int(nb.sum()) * Hq, "out_entries": Hq * B * W,
+            "flops": 2 * D * int(kv.sum()) * Hq,
+            "bytes": k_bytes + q_bytes + out_bytes + int(nb.sum()) * 4 + 8 * B,
+            "k_bytes": k_bytes, "q_bytes": q_bytes, "out_bytes": out_bytes}
+
+
+def bench_decode_batch(B: int, steps: int, warmup: int, seed: int = 20261299) -> dict:
+    """The bf16 decode workload's distribution at batch size B (kv_len ~
+    U[1, 32768], Hq = 16, Hkv = 1, MB = 256, B MB distinct pages in a random
+    table), keys drawn on the GPU from a seeded generator (host generation of
+    the 8.6 GB cache of B = 1024 would dominate the run).  Times the launch
+    with the drawn lengths (HBM roofline) and with every kv_len = 1, where
+    one block per request leaves the launch, the request lookup and the fill
+    of the unscored blocks."""
+    import ctypes
+    import numpy as np
+    import torch
+    import block_max_qk_amd as m
+    from block_max_qk_amd._binding import describe, LAYOUT_CODE
+
+    dev = torch.device("cuda:0")
+    Hq, Hkv, D, P, MB = 16, 1, 128, 128, 256
+    NP = B * MB
+    rng = np.random.default_rng(seed + B)
+    kv_np = rng.integers(1, 32768 + 1, size=B).astype(np.int64)
+    bt = torch.from_numpy(rng.permutation(NP)[: B * MB].reshape(B, MB).astype(np.int32)).to(dev)
+    g = torch.Generator(device=dev).manual_seed(seed + B)
+    key = torch.empty((NP, P, Hkv, D), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    q = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    W = m.msa_index_score_out_width(MB)
+    out = torch.empty((Hq, B, W), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = m.load_library()
+    qd, kd = describe(q), describe(key)
+
+    def timed(kv_host):
+        kv = torch.from_numpy(kv_host.astype(np.int32)).to(dev)
+        sl = torch.from_numpy(((kv_host - 1) // P).astype(np.int32)).to(dev)
+        a = (ctypes.byref(qd), ctypes.byref(kd), ctypes.c_void_p(sl.data_ptr()),
+             ctypes.c_void_p(bt.data_ptr()), MB, None, ctypes.c_void_p(cu.data_ptr()),
+             ctypes.c_void_p(kv.data_ptr()), B, P, LAYOUT_CODE["BBND"], 3, 0, 1, 0,
+             ctypes.c_void_p(out.data_ptr()), W, ctypes.c_void_p(stream.cuda_stream), -1)
+        for _ in range(warmup):
+            st = lib.msa_index_score_ex(*a)
+            if st != 0:
+                raise RuntimeError(m.msa_status_str(st))
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            lib.msa_index_score_ex(*a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(kv_np)
+    ms_one = timed(np.ones(B, dtype=np.int64))
+    st = decode_batch_stats(kv_np, Hq, Hkv, D, P, MB, 2)
+    gbs = st["bytes"] / (ms * 1e-3) / 1e9
+    fam = "decode" if m.msa_index_score_kernel_family(B, B, Hq, Hkv) == 0 else "prefill"
+    del key, out
+    torch.cuda.empty_cache()
+    return {"metric": "decode batch scaling", "config": {
+                "workload": f"decode_bbnd_bf16 distribution at B={B}", "B": B, "Hq": Hq,
+                "Hkv": Hkv, "D": D, "P": P, "MB": MB, "pages": NP, "kernel_family": fam,
+                "data": "synthetic, keys drawn on the GPU"},
+            "steps": steps, "warmup": warmup,
+            "kernel_ms_avg": round(ms, 5), "us_per_request": round(ms * 1e3 / B, 4),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": st["bytes"], "block_scores": st["scores"],
+            "kv_len_1_kernel_ms_avg": round(ms_one, 5),
+            "kv_len_1_us_per_request": round(ms_one * 1e3 / B, 4)}
+
+
 def workload_summary(r: dict) -> dict:
     """One workload's figures for the headline line's 'workloads' list."""
     keys = ("value", "unit", "ms_per_step", "dtype", "hbm_gbs", "mfma_tflops",
@@ -514,6 +602,9 @@ def main():
     ap.add_argument("--local-mode", choices=["request", "query"], default="request",
                     help="local_mask window at start_loc (the workloads' own setting) or at "
                          "each token's own block")
+    ap.add_argument("--decode-batch", default="",
+                    help="comma-separated batch sizes: time the bf16 decode workload's "
+                         "distribution at each (batch scaling of the request lookup)")
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="instead of the operator, run this many MiB device copies "
                          "(counter calibration)")
@@ -540,6 +631,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": n, "launches": max(args.steps, 1)}))
+        return
+
+    if args.decode_batch:
+        for b in [int(x) for x in args.decode_batch.split(",") if x]:
+            print(f"[bench] decode batch {b}", file=sys.stderr, flush=True)
+            print(json.dumps(bench_decode_batch(b, args.steps, args.warmup)), flush=True)
         return
 
     import synth

@@ -108,14 +108,12 @@ hipError_t launch_kernel(void (*kern)(KA...), dim3 grid, dim3 block, hipStream_t
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, 0, s);
 }
 
-template <int KK>
-hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
-  if (family == 1)
-    return launch_kernel(msa::prefill_kernel<KK>, dim3((unsigned)prefill_grid), dim3(256), s, p);
-  // Decode: one round of workgroups, as many as fit on the device at once,
-  // split evenly over the units (KV head x head chunk).  The device's slot
-  // count for this kernel is looked up once per device (the runtime queries
-  // cost microseconds, as much as a short decode launch).
+// Decode: one round of workgroups, as many as fit on the device at once,
+// split evenly over the units (KV head x head chunk).  The device's slot
+// count for each decode kernel is looked up once per device (the runtime
+// queries cost microseconds, as much as a short decode launch).
+template <int KK, bool BIG>
+hipError_t launch_decode(Params& p, hipStream_t s) {
   constexpr int kMaxDevices = 64;
   static std::atomic<int64_t> slots_of[kMaxDevices];
   int dev = 0;
@@ -127,13 +125,23 @@ hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
     int cus = 0, per_cu = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK>, 256, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK, BIG>, 256,
+                                                       0);
     if (e != hipSuccess) return e;
     slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     if (cached) slots_of[dev].store(slots, std::memory_order_relaxed);
   }
   const int64_t gu = std::max<int64_t>(1, slots / p.units);
-  return launch_kernel(msa::decode_kernel<KK>, dim3((unsigned)(gu * p.units)), dim3(256), s, p);
+  return launch_kernel(msa::decode_kernel<KK, BIG>, dim3((unsigned)(gu * p.units)), dim3(256), s,
+                       p);
+}
+
+template <int KK>
+hipError_t launch(int family, Params& p, int64_t prefill_grid, hipStream_t s) {
+  if (family == 1)
+    return launch_kernel(msa::prefill_kernel<KK>, dim3((unsigned)prefill_grid), dim3(256), s, p);
+  // batches of more than 64 requests: the kernel with the chunk table
+  return p.B > 64 ? launch_decode<KK, true>(p, s) : launch_decode<KK, false>(p, s);
 }
 
 msa_status_t run(const msa_tensor_t* query, const msa_tensor_t* key, const int32_t* start_loc,

@@ -134,6 +134,116 @@ __device__ __forceinline__ void count_work(const Params& p, Scan64& first, int& 
   }
 }
 
+// Batches of more than 64 requests: the work-list, tile and packed-key
+// offsets at the start of each 64-request chunk (the first kChunkTab chunks),
+// kept in LDS, so that a cursor is placed by one search over the table and
+// one scan of its chunk instead of a scan of the batch from its start.
+constexpr int kChunkTab = 256;
+struct ChunkTable {
+  int tasks[kChunkTab + 1];
+  int tiles[kChunkTab + 1];
+  int64_t kv[kChunkTab + 1];
+  int wave_tasks[4], wave_tiles[4];
+};
+
+// Totals over the batch (as count_work) and the chunk table: the four waves
+// scan every fourth chunk, then wave 0 turns the chunk totals into offsets.
+// Every wave of the workgroup calls it (it holds two workgroup barriers).
+__device__ __forceinline__ void count_work_table(const Params& p, ChunkTable& tab, int& ntask,
+                                                 int& ntile) {
+  const int wave = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int nch = (p.B + 63) >> 6;
+  const int ntab = min(nch, kChunkTab);
+  int wt = 0, wl = 0;
+  for (int ch = wave; ch < nch; ch += 4) {
+    const Scan64 s = scan64(p, ch << 6);
+    const int t = __shfl(s.inc_tasks, 63, 64);
+    const int u = __shfl(s.inc_tiles, 63, 64);
+    const int64_t kvt = __shfl(s.inc_kv, 63, 64);
+    if (ch < kChunkTab && l == 0) {
+      tab.tasks[ch + 1] = t;
+      tab.tiles[ch + 1] = u;
+      tab.kv[ch + 1] = kvt;
+    }
+    wt += t;
+    wl += u;
+  }
+  if (l == 0) {
+    tab.wave_tasks[wave] = wt;
+    tab.wave_tiles[wave] = wl;
+  }
+  __syncthreads();
+  ntask = tab.wave_tasks[0] + tab.wave_tasks[1] + tab.wave_tasks[2] + tab.wave_tasks[3];
+  ntile = tab.wave_tiles[0] + tab.wave_tiles[1] + tab.wave_tiles[2] + tab.wave_tiles[3];
+  if (wave == 0) {
+    int at = 0, al = 0;
+    int64_t ak = 0;
+    for (int base = 0; base < ntab; base += 64) {
+      const int e = base + l + 1;      // chunk e - 1's total, then chunk e's offset
+      const bool in = e <= ntab;
+      const int it = wave_incl_scan(in ? tab.tasks[e] : 0);
+      const int il = wave_incl_scan(in ? tab.tiles[e] : 0);
+      const int64_t ik = wave_incl_scan(in ? tab.kv[e] : (int64_t)0);
+      if (in) {
+        tab.tasks[e] = at + it;
+        tab.tiles[e] = al + il;
+        tab.kv[e] = ak + ik;
+      }
+      at += __shfl(it, 63, 64);
+      al += __shfl(il, 63, 64);
+      ak += __shfl(ik, 63, 64);
+    }
+    if (l == 0) {
+      tab.tasks[0] = 0;
+      tab.tiles[0] = 0;
+      tab.kv[0] = 0;
+    }
+  }
+  __syncthreads();
+}
+
+// seek() for batches with a chunk table: the scan starts at request base0
+// with the offsets acc0 (entries or tiles) and kacc0 (packed keys) before it.
+__device__ __forceinline__ void seek_from(const Params& p, int base0, int acc0, int64_t kacc0,
+                                          int tau, bool by_tile, Cursor& c) {
+  int acc = acc0;
+  int64_t kacc = kacc0;
+  for (int base = base0; base < p.B; base += 64) {
+    const Scan64 s = scan64(p, base);
+    const int cnt = by_tile ? s.tiles : s.tasks;
+    const int incl = by_tile ? s.inc_tiles : s.inc_tasks;
+    const int total = __shfl(incl, 63, 64);
+    if (tau < acc + total) {
+      const int src = __ffsll((long long)__ballot(acc + incl > tau)) - 1;
+      c.b = base + src;
+      c.Lq = __shfl(s.lq, src, 64);
+      c.L = __shfl(s.kv, src, 64);
+      c.koff = kacc + __shfl(s.inc_kv, src, 64) - c.L;
+      c.cu = __shfl(s.cu, src, 64);
+      int local = tau - (acc + __shfl(incl, src, 64) - __shfl(cnt, src, 64));
+      if (by_tile) {
+        c.j = local;
+        c.beta = 0;
+        c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
+        return;
+      }
+      for (int j = 0;; ++j) {
+        const int nv = tile_blocks(p, c.L, c.Lq, j);
+        if (local < nv) {
+          c.j = j;
+          c.beta = local;
+          c.nvis = nv;
+          return;
+        }
+        local -= nv;
+      }
+    }
+    acc += total;
+    kacc += __shfl(s.inc_kv, 63, 64);
+  }
+}
+
 // Cursor at work-list entry tau (< N).  With by_tile, tau counts tiles
 // instead and the cursor lands on block 0 of tile tau.
 __device__ __forceinline__ void seek(const Params& p, const Scan64& first, int tau,
@@ -175,6 +285,37 @@ __device__ __forceinline__ void seek(const Params& p, const Scan64& first, int t
   }
 }
 
+// The same through the chunk table: the last table chunk whose offset is at
+// most tau (the offsets do not decrease), then the scan from there.
+__device__ __forceinline__ void seek_table(const Params& p, const ChunkTable& tab, int tau,
+                                           bool by_tile, Cursor& c) {
+  const int ntab = min((p.B + 63) >> 6, kChunkTab);
+  const int* pre = by_tile ? tab.tiles : tab.tasks;
+  int ch = 0;
+  for (int base = 0; base < ntab; base += 64) {
+    const int e = base + lane_id();
+    const int cnt = __popcll(__ballot(e < ntab && pre[e] <= tau));
+    if (cnt > 0) ch = base + cnt - 1;
+    if (cnt < 64) break;
+  }
+  seek_from(p, ch << 6, pre[ch], tab.kv[ch], tau, by_tile, c);
+}
+
+// Move a cursor that sits on block 0 of a tile to block 0 of the next tile.
+__device__ __forceinline__ void next_tile(const Params& p, Cursor& c) {
+  ++c.j;
+  while (c.j >= tiles_of(p, c.Lq)) {
+    c.koff += c.L;
+    ++c.b;
+    c.cu = p.cu_q[c.b];
+    c.Lq = p.cu_q[c.b + 1] - c.cu;
+    c.L = consumed(p.kv_len[c.b]);
+    c.j = 0;
+  }
+  c.beta = 0;
+  c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
+}
+
 // Move the cursor `step` entries forward; the caller guarantees the target
 // entry exists.
 __device__ __forceinline__ void advance(const Params& p, Cursor& c, int step) {
@@ -211,7 +352,8 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
   return w;
 }
 
-template <int KK>
+// BIG: the batch has more than 64 requests (the chunk-table paths).
+template <int KK, bool BIG>
 __global__ __launch_bounds__(256, Kind<KK>::is_fp4 ? 4 : (Kind<KK>::is_i8 ? 3 : 2))
 void decode_kernel(Params p) {
   using Kd = Kind<KK>;
@@ -234,9 +376,21 @@ void decode_kernel(Params p) {
   const int hk = unit / p.hchunks;
   const int hc = unit - hk * p.hchunks;
 
+  // Batches of up to 64 requests keep their one chunk in registers; larger
+  // ones build the chunk table.
+  __shared__ std::conditional_t<BIG, ChunkTable, int> ctab;
   int ntask, ntile;
   Scan64 first;
-  count_work(p, first, ntask, ntile);
+  if constexpr (BIG)
+    count_work_table(p, ctab, ntask, ntile);
+  else
+    count_work(p, first, ntask, ntile);
+  auto place = [&](int tau, bool by_tile, Cursor& c) {
+    if constexpr (BIG)
+      seek_table(p, ctab, tau, by_tile, c);
+    else
+      seek(p, first, tau, by_tile, c);
+  };
 
   // Fill pass, run after the compute pass: the columns past each tile's last
   // visible block get -inf (and local_mask).  Items are (tile, row) pairs,
@@ -244,27 +398,64 @@ void decode_kernel(Params p) {
   // stores (a scalar head up to the first 16-byte boundary, which the compute
   // pass does not touch).  Run first, its stores and index reads delayed
   // every wave's first key loads by several microseconds.
-  auto fill_pass = [&]() {
-    for (int it = wi; it < ntile * kDecodeRows; it += gu) {
-      const int k = it / kDecodeRows;
-      const int r = it - k * kDecodeRows;
-      Cursor c;
-      seek(p, first, k, true, c);
-      const Work w = tile_work(p, c, hk, hc);
-      const int ri = r / p.hpt;
-      const int rh = hc * p.hpt + (r - ri * p.hpt);
-      if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
-      float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
-      const int start = local_anchor(p, w, c.j * p.tpt + ri);
-      const int v0 = c.nvis;
-      const int a0 = min((v0 + 3) & ~3, p.W);
-      if ((int)threadIdx.x < a0 - v0)
-        row[v0 + threadIdx.x] = finish(p, w.L, start, v0 + threadIdx.x, false, 0.f);
-      for (int cc = a0 + 4 * (int)threadIdx.x; cc < p.W; cc += 4 * 256) {
-        f32x4 v;
+  // With more than one chunk, each workgroup takes a contiguous range of
+  // items and steps its cursor from tile to tile instead of placing it anew
+  // for every item (which cost a scan per item).
+  auto fill_item = [&](const Cursor& c, int r) {
+    const Work w = tile_work(p, c, hk, hc);
+    const int ri = r / p.hpt;
+    const int rh = hc * p.hpt + (r - ri * p.hpt);
+    if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) return;
+    float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
+    const int start = local_anchor(p, w, c.j * p.tpt + ri);
+    const int v0 = c.nvis;
+    const int a0 = min((v0 + 3) & ~3, p.W);
+    if ((int)threadIdx.x < a0 - v0)
+      row[v0 + threadIdx.x] = finish(p, w.L, start, v0 + threadIdx.x, false, 0.f);
+    for (int cc = a0 + 4 * (int)threadIdx.x; cc < p.W; cc += 4 * 256) {
+      f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, start, cc + e, false, 0.f);
-        *reinterpret_cast<f32x4*>(row + cc) = v;
+      for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, start, cc + e, false, 0.f);
+      *reinterpret_cast<f32x4*>(row + cc) = v;
+    }
+  };
+  auto fill_pass = [&]() {
+    if constexpr (!BIG) {
+      for (int it = wi; it < ntile * kDecodeRows; it += gu) {
+        const int k = it / kDecodeRows;
+        const int r = it - k * kDecodeRows;
+        Cursor c;
+        seek(p, first, k, true, c);
+        const Work w = tile_work(p, c, hk, hc);
+        const int ri = r / p.hpt;
+        const int rh = hc * p.hpt + (r - ri * p.hpt);
+        if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
+        float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
+        const int start = local_anchor(p, w, c.j * p.tpt + ri);
+        const int v0 = c.nvis;
+        const int a0 = min((v0 + 3) & ~3, p.W);
+        if ((int)threadIdx.x < a0 - v0)
+          row[v0 + threadIdx.x] = finish(p, w.L, start, v0 + threadIdx.x, false, 0.f);
+        for (int cc = a0 + 4 * (int)threadIdx.x; cc < p.W; cc += 4 * 256) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, start, cc + e, false, 0.f);
+          *reinterpret_cast<f32x4*>(row + cc) = v;
+        }
+      }
+    } else {
+      const int nitems = ntile * kDecodeRows;
+      const int per = (nitems + gu - 1) / gu;
+      const int i0 = wi * per;
+      const int i1 = min(nitems, i0 + per);
+      if (i0 >= i1) return;
+      int ck = i0 / kDecodeRows;
+      Cursor c;
+      seek_table(p, ctab, ck, true, c);
+      for (int it = i0; it < i1; ++it) {
+        const int k = it / kDecodeRows;
+        for (; ck < k; ++ck) next_tile(p, c);
+        fill_item(c, it - k * kDecodeRows);
       }
     }
   };
@@ -280,7 +471,7 @@ void decode_kernel(Params p) {
   }
 
   Cursor c;
-  seek(p, first, task, false, c);
+  place(task, false, c);
   int cur_b = -1, cur_j = -1;
   Work w;
   i32x4 qv[4];

@@ -136,13 +136,14 @@ typedef struct {
  * block_table when batch = 0, and out when T = 0.
  *
  * Ownership: every pointer is caller-owned; the library allocates no device
- * memory.  The only state it keeps between calls is one figure per device
- * and key type: the decode kernel's workgroup slot count (CU count times
- * occupancy), asked of the HIP runtime on the first decode launch on that
- * device.  Returns MSA_OK or an error status; T = 0 returns MSA_OK without
- * launching anything.  MSA_ERR_HIP reports a failure of this call's own
- * runtime queries or launch, never an error pending from earlier HIP work.  query, key and
- * out must be 16-byte aligned and a paged key's dim0 stride a multiple of 16
+ * memory.  The only state it keeps between calls is one figure per device,
+ * key type and batch kind (at most 64 requests, or more): the decode
+ * kernel's workgroup slot count (CU count times occupancy), asked of the HIP
+ * runtime on the first such decode launch on that device.  Returns MSA_OK
+ * or an error status; T = 0 returns MSA_OK without launching anything.
+ * MSA_ERR_HIP reports a failure of this call's own runtime queries or
+ * launch, never an error pending from earlier HIP work.  query, key and out
+ * must be 16-byte aligned and a paged key's dim0 stride a multiple of 16
  * bytes (MSA_ERR_STRIDE otherwise).  Sizes past the kernels' 32-bit indexing
  * return MSA_ERR_SHAPE: out_width > 2^24, Hq > 2^16, batch > 2^30, T >= 2^31,
  * or one 128-token block of one head spanning 2 GiB or more of key memory.

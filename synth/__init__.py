@@ -15,6 +15,7 @@ from .inputs import (  # noqa: F401
     make_case,
     edge_cases,
     random_cases,
+    large_batch_cases,
     mx_random_cases,
     poison_case,
     case_summary,

@@ -573,6 +573,33 @@ def edge_cases() -> List[MsaCase]:
     return cs
 
 
+def large_batch_cases() -> List[MsaCase]:
+    """Batches of more than 64 requests (several 64-request chunks, the last
+    one past a 256-chunk table), with short lengths so the oracle stays quick:
+    one-token decode, speculative and empty requests, paged and packed keys."""
+    rng = np.random.default_rng(777)
+    out = []
+
+    def lens(B, lo, hi):
+        return [int(x) for x in rng.integers(lo, hi + 1, size=B)]
+
+    out.append(make_case("batch65_bbnd_bf16", 7001, q_lens=[1] * 65, kv_lens=lens(65, 0, 700),
+                         Hq=8, Hkv=1, qdtype="bf16", layout="BBND", sparse_mode=3,
+                         init_blocks=1, local_blocks=1))
+    out.append(make_case("batch300_bnbd_i8_spec", 7002,
+                         q_lens=[int(x) for x in rng.choice([0, 1, 2, 3], size=300)],
+                         kv_lens=lens(300, 0, 1000), Hq=16, Hkv=2, qdtype="f16", kdtype="i8",
+                         layout="BNBD", sparse_mode=3, init_blocks=0, local_blocks=2))
+    out.append(make_case("batch1000_tnd_f16", 7003, q_lens=[1] * 1000, kv_lens=lens(1000, 0, 400),
+                         Hq=4, Hkv=1, qdtype="f16", layout="TND", sparse_mode=3,
+                         init_blocks=1, local_blocks=1))
+    out.append(make_case("batch16500_tnd_bf16", 7004,
+                         q_lens=[int(x) for x in rng.choice([0, 1, 1, 1], size=16500)],
+                         kv_lens=lens(16500, 0, 200), Hq=2, Hkv=1, qdtype="bf16", layout="TND",
+                         sparse_mode=3, init_blocks=0, local_blocks=1))
+    return out
+
+
 def random_cases(n: int, seed: int = 4242) -> List[MsaCase]:
     """n small cases with every knob drawn at random (lengths, heads, key type,
     layout, mode, local_mask counts, table width, dim0 gap), for sweeps."""

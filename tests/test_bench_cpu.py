@@ -85,3 +85,15 @@ def test_cpu_baseline_legs():
 def test_per_token_visible_blocks_sum_to_the_score_count(idx):
     c = CASES[idx]
     assert int(bench.visible_blocks_per_token(c).sum()) * c.Hq == bench.workload_stats(c)["scores"]
+
+
+def test_decode_batch_stats_agree_with_workload_stats():
+    # the batch-scaling mode counts its work in closed form; on the bf16
+    # decode workload itself (same distribution, B = 64) it must agree with
+    # the general per-request count
+    c = synth.config_case(1)
+    want = bench.workload_stats(c)
+    got = bench.decode_batch_stats(c.kv_len.numpy(), c.Hq, c.Hkv, c.D, c.block_size,
+                                   c.max_blocks, 2)
+    for key in ("scores", "out_entries", "flops", "bytes", "k_bytes", "q_bytes", "out_bytes"):
+        assert got[key] == want[key], key

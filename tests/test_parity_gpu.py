@@ -108,6 +108,31 @@ def test_random_sweep_parity(idx, family, dev):
     assert r["ok"], r
 
 
+LARGE_BATCH_NAMES = ["batch65_bbnd_bf16", "batch300_bnbd_i8_spec", "batch1000_tnd_f16",
+                     "batch16500_tnd_bf16"]
+_LARGE = []
+
+
+def large_batch(idx):
+    # built on first use (about 2 GB of host tensors), not at collection
+    if not _LARGE:
+        _LARGE.extend(synth.large_batch_cases())
+        assert [c.name for c in _LARGE] == LARGE_BATCH_NAMES
+    return _LARGE[idx]
+
+
+@pytest.mark.parametrize("family", [0, 1])
+@pytest.mark.parametrize("idx", range(len(LARGE_BATCH_NAMES)), ids=LARGE_BATCH_NAMES)
+def test_large_batch_parity(idx, family, dev):
+    # more than one 64-request chunk: the decode kernel's chunk table and
+    # contiguous fill items, and the prefill request lookup, past 16384
+    # requests included
+    c = large_batch(idx)
+    log(f"[gpu] large batch {c.name} family={family} {synth.case_summary(c)}")
+    r = check(oracle_out(c), run_gpu(c, dev, family), tol_of(c))
+    assert r["ok"], r
+
+
 MX_RANDOM = synth.mx_random_cases(12)
 
 
