@@ -72,15 +72,40 @@ struct Params {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Inclusive prefix sum over the wave's 64 lanes, by DPP steps with no LDS
+// round trip: row_shr 1, 2, 4, 8 within each row of 16 lanes (a lane whose
+// source lies before its row adds 0), then row_bcast:15 adds lane 15's sum to
+// rows 1 and 3 and row_bcast:31 lane 31's to rows 2 and 3.  (Every lane of the
+// wave must be active.)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int64_t dpp_or_zero(int64_t v) {
+  const uint32_t lo = (uint32_t)dpp_or_zero<CTRL, ROWS>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)dpp_or_zero<CTRL, ROWS>((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    T y = __shfl_up(x, d, 64);
-    if (l >= d) x += y;
-  }
+  x += dpp_or_zero<0x111, 0xF>(x);
+  x += dpp_or_zero<0x112, 0xF>(x);
+  x += dpp_or_zero<0x114, 0xF>(x);
+  x += dpp_or_zero<0x118, 0xF>(x);
+  x += dpp_or_zero<0x142, 0xA>(x);
+  x += dpp_or_zero<0x143, 0xC>(x);
   return x;
+}
+
+// Lane src's value (src the same in every lane), through v_readlane.
+__device__ __forceinline__ int lane_at(int x, int src) {
+  return __builtin_amdgcn_readlane(x, src);
+}
+__device__ __forceinline__ int64_t lane_at(int64_t x, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Value of another lane in the same row of 16, by a DPP lane pattern.
@@ -116,6 +141,17 @@ __device__ __forceinline__ void wave_min_max(uint32_t x, uint32_t y, uint32_t& l
 __device__ __forceinline__ float max_xor32(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a);
+}
+
+// max(x[l], x[l ^ 16]) in every lane l: v_permlane16_swap exchanges the odd
+// rows (16 lanes each) of its first register with the even rows of its
+// second, so two copies of x become each row pair's two rows side by side,
+// and one v_max_f32 combines them (written out as max_xor32 is).
+__device__ __forceinline__ float max_xor16(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
                : "+v"(a), "+v"(b));
   return __builtin_bit_cast(float, a);
 }
@@ -228,17 +264,17 @@ __device__ __forceinline__ Work locate(const Params& p) {
     const int n = (lq + p.tpt - 1) / p.tpt;
     const int incl = wave_incl_scan(n);
     const int64_t kincl = wave_incl_scan((int64_t)kv);
-    const int total = __shfl(incl, 63, 64);
+    const int total = lane_at(incl, 63);
     if (tile < acc + total) {
       const unsigned long long m = __ballot(acc + incl > tile);
       const int src = __ffsll((long long)m) - 1;
-      const int n_s = __shfl(n, src, 64);
-      const int incl_s = __shfl(incl, src, 64);
-      const int kv_s = __shfl(kv, src, 64);
-      const int64_t kincl_s = __shfl(kincl, src, 64);
+      const int n_s = lane_at(n, src);
+      const int incl_s = lane_at(incl, src);
+      const int kv_s = lane_at(kv, src);
+      const int64_t kincl_s = lane_at(kincl, src);
       w.b = base + src;
       const int tin = tile - (acc + incl_s - n_s);
-      w.Lq = __shfl(lq, src, 64);
+      w.Lq = lane_at(lq, src);
       w.L = kv_s;
       w.t0 = p.cu_q[w.b] + tin * p.tpt;
       w.ntok = min(p.tpt, w.Lq - tin * p.tpt);
@@ -247,7 +283,7 @@ __device__ __forceinline__ Work locate(const Params& p) {
       return w;
     }
     acc += total;
-    kacc += __shfl(kincl, 63, 64);
+    kacc += lane_at(kincl, 63);
   }
   return w;
 }

@@ -129,8 +129,8 @@ __device__ __forceinline__ void count_work(const Params& p, Scan64& first, int& 
   for (int base = 0; base < p.B; base += 64) {
     const Scan64 s = scan64(p, base);
     if (base == 0) first = s;
-    ntask += __shfl(s.inc_tasks, 63, 64);
-    ntile += __shfl(s.inc_tiles, 63, 64);
+    ntask += lane_at(s.inc_tasks, 63);
+    ntile += lane_at(s.inc_tiles, 63);
   }
 }
 
@@ -158,9 +158,9 @@ __device__ __forceinline__ void count_work_table(const Params& p, ChunkTable& ta
   int wt = 0, wl = 0;
   for (int ch = wave; ch < nch; ch += 4) {
     const Scan64 s = scan64(p, ch << 6);
-    const int t = __shfl(s.inc_tasks, 63, 64);
-    const int u = __shfl(s.inc_tiles, 63, 64);
-    const int64_t kvt = __shfl(s.inc_kv, 63, 64);
+    const int t = lane_at(s.inc_tasks, 63);
+    const int u = lane_at(s.inc_tiles, 63);
+    const int64_t kvt = lane_at(s.inc_kv, 63);
     if (ch < kChunkTab && l == 0) {
       tab.tasks[ch + 1] = t;
       tab.tiles[ch + 1] = u;
@@ -190,9 +190,9 @@ __device__ __forceinline__ void count_work_table(const Params& p, ChunkTable& ta
         tab.tiles[e] = al + il;
         tab.kv[e] = ak + ik;
       }
-      at += __shfl(it, 63, 64);
-      al += __shfl(il, 63, 64);
-      ak += __shfl(ik, 63, 64);
+      at += lane_at(it, 63);
+      al += lane_at(il, 63);
+      ak += lane_at(ik, 63);
     }
     if (l == 0) {
       tab.tasks[0] = 0;
@@ -213,15 +213,15 @@ __device__ __forceinline__ void seek_from(const Params& p, int base0, int acc0, 
     const Scan64 s = scan64(p, base);
     const int cnt = by_tile ? s.tiles : s.tasks;
     const int incl = by_tile ? s.inc_tiles : s.inc_tasks;
-    const int total = __shfl(incl, 63, 64);
+    const int total = lane_at(incl, 63);
     if (tau < acc + total) {
       const int src = __ffsll((long long)__ballot(acc + incl > tau)) - 1;
       c.b = base + src;
-      c.Lq = __shfl(s.lq, src, 64);
-      c.L = __shfl(s.kv, src, 64);
-      c.koff = kacc + __shfl(s.inc_kv, src, 64) - c.L;
-      c.cu = __shfl(s.cu, src, 64);
-      int local = tau - (acc + __shfl(incl, src, 64) - __shfl(cnt, src, 64));
+      c.Lq = lane_at(s.lq, src);
+      c.L = lane_at(s.kv, src);
+      c.koff = kacc + lane_at(s.inc_kv, src) - c.L;
+      c.cu = lane_at(s.cu, src);
+      int local = tau - (acc + lane_at(incl, src) - lane_at(cnt, src));
       if (by_tile) {
         c.j = local;
         c.beta = 0;
@@ -240,7 +240,7 @@ __device__ __forceinline__ void seek_from(const Params& p, int base0, int acc0, 
       }
     }
     acc += total;
-    kacc += __shfl(s.inc_kv, 63, 64);
+    kacc += lane_at(s.inc_kv, 63);
   }
 }
 
@@ -254,15 +254,15 @@ __device__ __forceinline__ void seek(const Params& p, const Scan64& first, int t
     const Scan64 s = base == 0 ? first : scan64(p, base);
     const int cnt = by_tile ? s.tiles : s.tasks;
     const int incl = by_tile ? s.inc_tiles : s.inc_tasks;
-    const int total = __shfl(incl, 63, 64);
+    const int total = lane_at(incl, 63);
     if (tau < acc + total) {
       const int src = __ffsll((long long)__ballot(acc + incl > tau)) - 1;
       c.b = base + src;
-      c.Lq = __shfl(s.lq, src, 64);
-      c.L = __shfl(s.kv, src, 64);
-      c.koff = kacc + __shfl(s.inc_kv, src, 64) - c.L;
-      c.cu = __shfl(s.cu, src, 64);
-      int local = tau - (acc + __shfl(incl, src, 64) - __shfl(cnt, src, 64));
+      c.Lq = lane_at(s.lq, src);
+      c.L = lane_at(s.kv, src);
+      c.koff = kacc + lane_at(s.inc_kv, src) - c.L;
+      c.cu = lane_at(s.cu, src);
+      int local = tau - (acc + lane_at(incl, src) - lane_at(cnt, src));
       if (by_tile) {
         c.j = local;
         c.beta = 0;
@@ -281,7 +281,7 @@ __device__ __forceinline__ void seek(const Params& p, const Scan64& first, int t
       }
     }
     acc += total;
-    kacc += __shfl(s.inc_kv, 63, 64);
+    kacc += lane_at(s.inc_kv, 63);
   }
 }
 
@@ -720,9 +720,9 @@ void decode_kernel(Params p) {
       if (pend_ok) *pend_ptr = pend_val;
       m = full ? score(std::false_type{}) : score(std::true_type{});
     }
-    // the four k groups hold disjoint key tokens of the same row
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    // the four k groups (lanes n + 16 G) hold disjoint key tokens of the
+    // same row
+    m = max_xor32(max_xor16(m));
     pend_ok = G == 0 && row_ok;
     pend_ptr = p.out + (((int64_t)hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W + beta;
     pend_val = finish(p, w.L, start, beta, true, m);
