@@ -393,9 +393,6 @@ msa_status_t msa_index_score_ex(const msa_tensor_t* query, const msa_tensor_t* k
              local_blocks, local_mode, out, out_width, stream, family, false);
 }
 
-#ifndef MSA_TOPK_R4_FULL16
-#define MSA_TOPK_R4_FULL16 0
-#endif
 msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t width,
                             int64_t num_valid, int32_t k, int32_t* out, void* stream) {
   if (Hq < 0 || T < 0 || width < 0 || width > (1 << 24) || num_valid < 0 || num_valid > width)
@@ -415,7 +412,7 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   // (each row's loads overlap the selection on the row before); few rows
   // keep one per wave, for parallelism, and so do longer rows, where a
   // second row's registers would cost occupancy.
-  const int R = Hq * T >= (int64_t)msa::kTopkManyRows && (nv <= 512 || nv == MSA_TOPK_R4_FULL16) ? 4 : 1;
+  const int R = Hq * T >= (int64_t)msa::kTopkManyRows && nv <= 512 ? 4 : 1;
   const dim3 grid((unsigned)((T + msa::kTopkWaves * R - 1) / (msa::kTopkWaves * R)), (unsigned)Hq);
   const dim3 block(64 * msa::kTopkWaves);
   hipError_t e;
@@ -439,9 +436,7 @@ msa_status_t msa_block_topk(const float* scores, int64_t Hq, int64_t T, int64_t 
   } else if (nv <= 512) {
     MSA_TOPK_LAUNCH(8);
   } else if (nv <= 1024) {
-    if (nv == 1024 && R == 4)
-      MSA_TOPK_GO(16, 4, true);
-    else if (nv == 1024)
+    if (nv == 1024)
       MSA_TOPK_GO(16, 1, true);
     else
       MSA_TOPK_GO(16, 1, false);

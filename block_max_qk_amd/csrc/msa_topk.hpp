@@ -28,9 +28,17 @@
 namespace msa {
 
 constexpr int kTopkMax = 64;   // k is at most one wave of lanes
-// A wave's LDS area holds 128 entries: 64 compacted ones, then a spare entry
-// per lane for the stores of lanes with nothing to compact.
+// A wave's LDS area holds 64 compacted entries, then a spare entry per lane
+// for the stores of lanes with nothing to compact: 128 entries.  Rows held in
+// up to 8 registers per lane get room for every key of the row (64 J
+// entries, then the spare ones), so their compaction needs no bound on its
+// store positions (4.6 KB per wave at J = 8, which still leaves eight waves
+// per SIMD).
 constexpr int kTopkSpare = 64;
+template <int J>
+constexpr bool topk_roomy() { return J > 0 && J <= 8; }
+template <int J>
+constexpr int topk_area_entries() { return topk_roomy<J>() ? 64 * J + 64 : 128; }
 
 // Order-preserving key of a score that can be selected; 0 for -inf and NaN.
 __device__ __forceinline__ uint32_t topk_key(float f) {
@@ -50,7 +58,7 @@ constexpr int64_t kTopkManyRows = 65536;
 
 // The threshold search on one row.  J > 0: keys[j] in lane l is the key
 // (topk_key, 0 past nv) of block 64 j + l.  J = 0 re-reads the row.
-// slot: this wave's 128-entry LDS area; sel: its 64-entry output area.  The
+// slot: this wave's LDS area (at least 128 entries); sel: its 64-entry output area.  The
 // k results go to dst with one store per lane (lanes past k repeat slot k - 1),
 // so every row issues the same memory operations.
 template <int J>
@@ -332,19 +340,21 @@ __device__ __forceinline__ bool topk_row_fast(const float (&x)[J], int k,
   const float t0f = topk_key_rot_score(t0);
 
   // compaction of the keys >= t0, in index order, as (key, block) entries.
-  // Each store goes to the area's byte address 8 min(base, 64) (scalar) plus
-  // 8 times the lane's rank in the chunk; lanes whose key does not qualify
-  // write to their spare entry, so the stores need no branch.  A row with
-  // more than 64 such keys goes to the general search; until this pass ends
-  // its stores stay inside the area (index at most 64 + 63).
+  // Each store goes to the area's byte address 8 base (scalar; 8 min(base,
+  // 64) in a 128-entry area) plus 8 times the lane's rank in the chunk;
+  // lanes whose key does not qualify write to their spare entry, so the
+  // stores need no branch.  A row with more than 64 such keys goes to the
+  // general search; until this pass ends its stores stay inside the area
+  // (index at most 64 J - 1, or 64 + 63 in a 128-entry area).
   // (For J > 8 the lane number passes through an empty asm, so that the
   // block numbers are formed at each store rather than held in registers
   // across rows.)
   uint32_t lv = (uint32_t)l;
   if constexpr (J > 8) asm volatile("" : "+v"(lv));
+  constexpr bool ROOMY = topk_roomy<J>();
   char* const area = reinterpret_cast<char*>(slot);
   char* const area_end = area + 8 * 64;
-  uint2* const spare = slot + kTopkSpare + l;
+  uint2* const spare = slot + (ROOMY ? 64 * J : kTopkSpare) + l;
   char* next = area;                         // area + 8 (entries so far)
 #pragma unroll
   for (int j = 0; j < J; ++j) {
@@ -352,7 +362,8 @@ __device__ __forceinline__ bool topk_row_fast(const float (&x)[J], int k,
     const uint64_t mk = __ballot(q);
     const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    uint2* const at = reinterpret_cast<uint2*>(next < area_end ? next : area_end) + r;
+    uint2* const at =
+        reinterpret_cast<uint2*>(ROOMY ? next : (next < area_end ? next : area_end)) + r;
     *(q ? at : spare) = make_uint2(__float_as_uint(x[j]), lv + (uint32_t)(j * 64));
     next += 8 * __popcll(mk);
   }
@@ -484,7 +495,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       if (l < k) dst_of(i)[l] = -1;
     return;
   }
-  __shared__ uint2 packed[kTopkWaves][128];
+  __shared__ uint2 packed[kTopkWaves][topk_area_entries<J>()];
   __shared__ int32_t chosen[kTopkWaves][64];
   const float* const row0 = scores + (h * T + t0) * W;
   auto row_of = [&](int i) { return row0 + min(i, last) * (int)W; };
