@@ -593,6 +593,10 @@ def large_batch_cases() -> List[MsaCase]:
     out.append(make_case("batch1000_tnd_f16", 7003, q_lens=[1] * 1000, kv_lens=lens(1000, 0, 400),
                          Hq=4, Hkv=1, qdtype="f16", layout="TND", sparse_mode=3,
                          init_blocks=1, local_blocks=1))
+    out.append(make_case("batch200_bbnd_f16_perq", 7005,
+                         q_lens=[int(x) for x in rng.choice([1, 2, 5], size=200)],
+                         kv_lens=lens(200, 0, 900), Hq=8, Hkv=2, qdtype="f16", layout="BBND",
+                         sparse_mode=3, init_blocks=1, local_blocks=2, local_mode=1))
     out.append(make_case("batch16500_tnd_bf16", 7004,
                          q_lens=[int(x) for x in rng.choice([0, 1, 1, 1], size=16500)],
                          kv_lens=lens(16500, 0, 200), Hq=2, Hkv=1, qdtype="bf16", layout="TND",

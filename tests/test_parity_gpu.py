@@ -109,7 +109,7 @@ def test_random_sweep_parity(idx, family, dev):
 
 
 LARGE_BATCH_NAMES = ["batch65_bbnd_bf16", "batch300_bnbd_i8_spec", "batch1000_tnd_f16",
-                     "batch16500_tnd_bf16"]
+                     "batch200_bbnd_f16_perq", "batch16500_tnd_bf16"]
 _LARGE = []
 
 
