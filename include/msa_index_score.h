@@ -249,7 +249,8 @@ msa_status_t msa_index_score_mxfp4_family(const msa_tensor_t* query, const uint8
  * of the row scores[h, t, :] whose score is above -inf (NaN never qualifies),
  * the k with the highest scores, equal scores taken by lower block index,
  * are written to out[t, h, 0:k] in ascending block order; the slots past the
- * number selected hold -1.  Selection works on the raw scores.
+ * number selected hold -1.  Selection works on the raw scores, compared as
+ * floats (so -0.0 and +0.0 are equal scores).
  *
  * scores     device float32 [Hq, T, width], compact (msa_index_score's out),
  *            4-byte aligned; not read when num_valid = 0.
