@@ -1146,6 +1146,28 @@ void prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
       f32x16 acc[NTW];
+      // MXFP4: two accumulator sets, M tiles alternating; an M tile's
+      // maxima are taken while the next tile's MFMAs run (half of its N
+      // tiles after each of the next tile's two fragments), so that each
+      // wave's vector work overlaps its own matrix work
+      static_assert(!Kd::is_fp4 || PER_MT == 2, "MXFP4 epilogue halves assume two fragments per M tile");
+      f32x16 acc2[Kd::is_fp4 ? 2 : 1][Kd::is_fp4 ? NTW : 1];
+      auto tile_max = [&](const f32x16 (&a)[Kd::is_fp4 ? NTW : 1], int mt, int nt0, int nt1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jr = off + mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+#pragma unroll
+          for (int nt = 0; nt < (Kd::is_fp4 ? NTW : 1); ++nt) {
+            if (nt < nt0 || nt >= nt1) continue;
+            float v = a[nt][r];
+            if constexpr (MASKED) {
+              const int j = beta * kP + jr;
+              v = (j <= lim[nt]) ? v : -__builtin_inff();
+            }
+            run[nt] = fmaxf(run[nt], v);
+          }
+        }
+      };
       // MXFP4: this block's scale words, token 32 mt + n in word mt
       uint32_t ksw[Kd::is_fp4 ? 4 : 1];
       if constexpr (Kd::is_fp4) {
@@ -1170,16 +1192,28 @@ void prefill_kernel(Params p) {
         }
         if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
         const int mt = i / PER_MT, q = i % PER_MT;
-        if (q == 0) {
+        if (!Kd::is_fp4 && q == 0) {
 #pragma unroll
           for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x16{};
         }
         if constexpr (Kd::is_fp4) {
           // byte 2q + G of the token's scale word is this lane's group
           const int sa = (ksw[mt] >> (8 * (2 * q + G))) & 255;
+          f32x16 (&ac)[NTW] = acc2[mt & 1];
+          if (q == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) ac[nt] = f32x16{};
+          }
 #pragma unroll
           for (int nt = 0; nt < NTW; ++nt)
-            acc[nt] = mfma32x32x64_fp4(f[i], qv[nt][q], acc[nt], sa, qsc[nt][q]);
+            ac[nt] = mfma32x32x64_fp4(f[i], qv[nt][q], ac[nt], sa, qsc[nt][q]);
+          if (mt > 0) {
+            if (q == 0)
+              tile_max(acc2[(mt - 1) & 1], mt - 1, 0, NTW / 2);
+            else
+              tile_max(acc2[(mt - 1) & 1], mt - 1, NTW / 2, NTW);
+          }
+          if (i == NFR - 1) tile_max(ac, mt, 0, NTW);
         } else if constexpr (Kd::is_f8) {
           if (q & 1) {
             const int s = q >> 1;
@@ -1193,7 +1227,7 @@ void prefill_kernel(Params p) {
           for (int nt = 0; nt < NTW; ++nt)
             acc[nt] = mfma32x32x16<Kd::mfma_kind>(f[i], qv[nt][q], acc[nt]);
         }
-        if (q == PER_MT - 1) {
+        if (!Kd::is_fp4 && q == PER_MT - 1) {
           // acc[nt][r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
