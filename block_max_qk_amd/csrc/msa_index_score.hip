@@ -114,6 +114,7 @@ hipError_t launch_kernel(void (*kern)(KA...), dim3 grid, dim3 block, hipStream_t
 // queries cost microseconds, as much as a short decode launch).
 template <int KK, bool BIG>
 hipError_t launch_decode(Params& p, hipStream_t s) {
+  constexpr int kThreads = 64 * msa::decode_waves<KK, BIG>();
   constexpr int kMaxDevices = 64;
   static std::atomic<int64_t> slots_of[kMaxDevices];
   int dev = 0;
@@ -125,15 +126,15 @@ hipError_t launch_decode(Params& p, hipStream_t s) {
     int cus = 0, per_cu = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK, BIG>, 256,
-                                                       0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, msa::decode_kernel<KK, BIG>,
+                                                       kThreads, 0);
     if (e != hipSuccess) return e;
     slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     if (cached) slots_of[dev].store(slots, std::memory_order_relaxed);
   }
   const int64_t gu = std::max<int64_t>(1, slots / p.units);
-  return launch_kernel(msa::decode_kernel<KK, BIG>, dim3((unsigned)(gu * p.units)), dim3(256), s,
-                       p);
+  return launch_kernel(msa::decode_kernel<KK, BIG>, dim3((unsigned)(gu * p.units)),
+                       dim3(kThreads), s, p);
 }
 
 template <int KK>

@@ -10,9 +10,9 @@
 //
 // decode_kernel  -- 16 rows per tile (the g heads of a KV group for one or a
 //   few tokens).  Key traffic dominates and nothing is reused across rows, so
-//   each of the four waves streams whole blocks straight from HBM into MFMA
-//   operand registers (16x16 tiles, key tokens on M, rows on N) and many
-//   waves per CU keep enough bytes in flight.
+//   each wave streams whole blocks straight from HBM into MFMA operand
+//   registers (16x16 tiles, key tokens on M, rows on N) and many waves per CU
+//   keep enough bytes in flight.
 // prefill_kernel -- 384 rows per tile for 16-bit keys (48 tokens x 8 heads for
 //   g = 8), 256 for fp8 and int8.  A key block is staged once per workgroup
 //   into LDS in a bank-conflict-free XOR-swizzled layout (straight from
@@ -62,11 +62,14 @@ constexpr int prefill_rows(int kk) { return 4 * 32 * prefill_ntw(kk); }
 //
 // The batch's work is the list of (tile, visible block) pairs, tiles in
 // request order and blocks ascending; its length N is known only on the
-// device.  Each workgroup takes an equal contiguous slice of the list and its
-// four waves take every fourth pair of the slice, so every wave streams about
-// the same number of key blocks whatever the spread of kv_len.  The grid is
-// one round of workgroups (as many as the chip holds at once), so no
-// workgroup waits for a slot.  Columns a tile cannot see (past its last
+// device.  Each workgroup takes an equal contiguous slice of the list, so
+// every CU streams about the same number of key blocks whatever the spread
+// of kv_len.  With at most 64 requests a workgroup holds all of a CU's waves
+// and they take the slice's pairs from an LDS counter as they finish blocks;
+// with more, four-wave workgroups (two to four per CU) and each wave takes
+// every fourth pair of its workgroup's slice.  The grid is one round of
+// workgroups (as many as the chip holds at once), so no workgroup waits for
+// a slot.  Columns a tile cannot see (past its last
 // visible block, up to the output width) are written by a fill pass.
 // Key blocks are loaded to registers: 16-bit, fp8 and int8 blocks pass
 // through a per-wave LDS area into the MFMA operand order; MXFP4 blocks
@@ -98,20 +101,24 @@ struct Cursor {
 
 // Per-lane view of 64 consecutive requests: lengths, their work-list and
 // tile counts, and wave-wide inclusive prefix sums of those.
+// With SL, also each request's start_loc (0 under the per-query window, where
+// it is not read).
 struct Scan64 {
-  int cu, lq, kv, tasks, tiles;
+  int cu, lq, kv, sl, tasks, tiles;
   int inc_tasks, inc_tiles;
   int64_t inc_kv;
 };
 
+template <bool SL = false>
 __device__ __forceinline__ Scan64 scan64(const Params& p, int base) {
   Scan64 s;
   const int b = base + lane_id();
-  s.cu = s.lq = s.kv = s.tasks = s.tiles = 0;
+  s.cu = s.lq = s.kv = s.sl = s.tasks = s.tiles = 0;
   if (b < p.B) {
     s.cu = p.cu_q[b];
     s.lq = p.cu_q[b + 1] - s.cu;
     s.kv = p.kv_len[b];
+    if (SL && !p.local_per_query) s.sl = p.start_loc[b];
     s.tiles = tiles_of(p, s.lq);
     for (int j = 0; j < s.tiles; ++j) s.tasks += tile_blocks(p, s.kv, s.lq, j);
   }
@@ -127,7 +134,7 @@ __device__ __forceinline__ void count_work(const Params& p, Scan64& first, int& 
                                            int& ntile) {
   ntask = ntile = 0;
   for (int base = 0; base < p.B; base += 64) {
-    const Scan64 s = scan64(p, base);
+    const Scan64 s = scan64<true>(p, base);
     if (base == 0) first = s;
     ntask += lane_at(s.inc_tasks, 63);
     ntile += lane_at(s.inc_tiles, 63);
@@ -244,44 +251,35 @@ __device__ __forceinline__ void seek_from(const Params& p, int base0, int acc0, 
   }
 }
 
-// Cursor at work-list entry tau (< N).  With by_tile, tau counts tiles
+// Cursor at work-list entry tau (< N) of a batch of at most 64 requests,
+// whose scan is `first`: no memory reads.  With by_tile, tau counts tiles
 // instead and the cursor lands on block 0 of tile tau.
 __device__ __forceinline__ void seek(const Params& p, const Scan64& first, int tau,
                                      bool by_tile, Cursor& c) {
-  int acc = 0;
-  int64_t kacc = 0;
-  for (int base = 0; base < p.B; base += 64) {
-    const Scan64 s = base == 0 ? first : scan64(p, base);
-    const int cnt = by_tile ? s.tiles : s.tasks;
-    const int incl = by_tile ? s.inc_tiles : s.inc_tasks;
-    const int total = lane_at(incl, 63);
-    if (tau < acc + total) {
-      const int src = __ffsll((long long)__ballot(acc + incl > tau)) - 1;
-      c.b = base + src;
-      c.Lq = lane_at(s.lq, src);
-      c.L = lane_at(s.kv, src);
-      c.koff = kacc + lane_at(s.inc_kv, src) - c.L;
-      c.cu = lane_at(s.cu, src);
-      int local = tau - (acc + lane_at(incl, src) - lane_at(cnt, src));
-      if (by_tile) {
-        c.j = local;
-        c.beta = 0;
-        c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
-        return;
-      }
-      for (int j = 0;; ++j) {
-        const int nv = tile_blocks(p, c.L, c.Lq, j);
-        if (local < nv) {
-          c.j = j;
-          c.beta = local;
-          c.nvis = nv;
-          return;
-        }
-        local -= nv;
-      }
+  const int cnt = by_tile ? first.tiles : first.tasks;
+  const int incl = by_tile ? first.inc_tiles : first.inc_tasks;
+  const int src = __ffsll((long long)__ballot(incl > tau)) - 1;
+  c.b = src;
+  c.Lq = lane_at(first.lq, src);
+  c.L = lane_at(first.kv, src);
+  c.koff = lane_at(first.inc_kv, src) - c.L;
+  c.cu = lane_at(first.cu, src);
+  int local = tau - (lane_at(incl, src) - lane_at(cnt, src));
+  if (by_tile) {
+    c.j = local;
+    c.beta = 0;
+    c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
+    return;
+  }
+  for (int j = 0;; ++j) {
+    const int nv = tile_blocks(p, c.L, c.Lq, j);
+    if (local < nv) {
+      c.j = j;
+      c.beta = local;
+      c.nvis = nv;
+      return;
     }
-    acc += total;
-    kacc += lane_at(s.inc_kv, 63);
+    local -= nv;
   }
 }
 
@@ -335,6 +333,43 @@ __device__ __forceinline__ void advance(const Params& p, Cursor& c, int step) {
   }
 }
 
+// advance() for a batch of at most 64 requests, whose lengths the scan
+// `first` holds: no memory reads.
+__device__ __forceinline__ void advance_scan(const Params& p, const Scan64& f, Cursor& c,
+                                             int step) {
+  c.beta += step;
+  while (c.beta >= c.nvis) {
+    c.beta -= c.nvis;
+    ++c.j;
+    while (c.j >= tiles_of(p, c.Lq)) {
+      c.koff += c.L;
+      ++c.b;
+      c.cu = lane_at(f.cu, c.b);
+      c.Lq = lane_at(f.lq, c.b);
+      c.L = lane_at(f.kv, c.b);
+      c.j = 0;
+    }
+    c.nvis = tile_blocks(p, c.L, c.Lq, c.j);
+  }
+}
+
+// Waves per decode workgroup.  A batch of at most 64 requests runs one
+// workgroup per CU holding all of the CU's waves (two per SIMD for 16-bit
+// keys, three for int8 and fp8, four for MXFP4), which share the workgroup's
+// slice of the work list through an LDS counter; the chunk-table instance
+// (larger batches) runs four-wave workgroups with fixed shares.
+template <int KK, bool BIG>
+constexpr int decode_waves() {
+  return BIG ? 4
+             : 4 * (Kind<KK>::is_fp4 ? 4 : (Kind<KK>::is_i8 || Kind<KK>::is_f8) ? 3 : 2);
+}
+
+// Workgroups per CU the decode kernel is built for (its register budget).
+template <int KK, bool BIG>
+constexpr int decode_min_groups() {
+  return BIG ? (Kind<KK>::is_fp4 ? 4 : (Kind<KK>::is_i8 ? 3 : 2)) : 1;
+}
+
 // Work of the cursor's tile as seen by the block helpers.
 __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int hk, int hc) {
   Work w;
@@ -354,21 +389,33 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
 
 // BIG: the batch has more than 64 requests (the chunk-table paths).
 template <int KK, bool BIG>
-__global__ __launch_bounds__(256, Kind<KK>::is_fp4 ? 4 : (Kind<KK>::is_i8 ? 3 : 2))
+__global__ __launch_bounds__((64 * decode_waves<KK, BIG>()), (decode_min_groups<KK, BIG>()))
 void decode_kernel(Params p) {
   using Kd = Kind<KK>;
+  constexpr int NW = decode_waves<KK, BIG>();
   // int8: each wave's current block of column scales, staged so that every
   // lane can read the four consecutive scales of its accumulator tokens
-  __shared__ __attribute__((aligned(16))) float dscl[Kd::is_i8 ? 4 : 1][kP];
+  __shared__ __attribute__((aligned(16))) float dscl[Kd::is_i8 ? NW : 1][kP];
   // four transpose areas per wave, each one 16-token sub-tile of key rows
   // (MXFP4 reads its operands straight from memory and uses none)
   constexpr int RBY = kD * Kd::k_bytes;        // key row bytes
-  __shared__ __attribute__((aligned(16))) uint8_t dkt[Kd::is_fp4 ? 1 : 4][Kd::is_fp4 ? 1 : 4]
+  __shared__ __attribute__((aligned(16))) uint8_t dkt[Kd::is_fp4 ? 1 : NW][Kd::is_fp4 ? 1 : 4]
                                                      [Kd::is_fp4 ? 16 : 16 * RBY];
+  // Batches of at most 64 requests: the two counters the waves take entries
+  // from (blocks of the workgroup's slice, then its fill items).
+  __shared__ int ctr[BIG ? 1 : 2];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int n = l & 15;          // this lane's row (MFMA N index) and key token (M index)
   const int G = l >> 4;          // this lane's k group, 0..3
+  if constexpr (!BIG) {
+    // (before any wave takes an entry; every wave passes this barrier)
+    if (threadIdx.x == 0) {
+      ctr[0] = NW;
+      ctr[1] = NW;
+    }
+    __syncthreads();
+  }
 
   const int unit = blockIdx.x % p.units;
   const int wi = blockIdx.x / p.units;
@@ -391,28 +438,37 @@ void decode_kernel(Params p) {
     else
       seek(p, first, tau, by_tile, c);
   };
+  // last block of a row's local_mask window (the scan holds start_loc when
+  // the batch has at most 64 requests)
+  auto anchor = [&](const Work& w, int i) -> int {
+    if constexpr (BIG)
+      return local_anchor(p, w, i);
+    else
+      return p.local_per_query ? query_anchor(w, i) : lane_at(first.sl, w.b);
+  };
 
-  // Fill pass, run after the compute pass: the columns past each tile's last
-  // visible block get -inf (and local_mask).  Items are (tile, row) pairs,
-  // dealt to the workgroups in turn; a row's columns are written as 16-byte
-  // stores (a scalar head up to the first 16-byte boundary, which the compute
-  // pass does not touch).  Run first, its stores and index reads delayed
-  // every wave's first key loads by several microseconds.
-  // With more than one chunk, each workgroup takes a contiguous range of
-  // items and steps its cursor from tile to tile instead of placing it anew
-  // for every item (which cost a scan per item).
-  auto fill_item = [&](const Cursor& c, int r) {
+  // Fill, after the compute pass: the columns past each tile's last visible
+  // block get -inf (and local_mask).  Items are (tile, row) pairs; each
+  // workgroup takes a contiguous range of them.  A row's columns are written
+  // as 16-byte stores (a scalar head up to the first 16-byte boundary, which
+  // the compute pass does not touch).  Run first, its stores and index reads
+  // delayed every wave's first key loads by several microseconds.  With the
+  // chunk table the whole workgroup writes each item in turn, its cursor
+  // stepped from tile to tile (placing it anew for every item cost a scan per
+  // item); with at most 64 requests each wave takes items from an LDS counter
+  // once it runs out of blocks, so the waves that finish last take none.
+  auto fill_item = [&](const Cursor& c, int r, int tix, int nthr) {
     const Work w = tile_work(p, c, hk, hc);
     const int ri = r / p.hpt;
     const int rh = hc * p.hpt + (r - ri * p.hpt);
     if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) return;
     float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
-    const int start = local_anchor(p, w, c.j * p.tpt + ri);
+    const int start = anchor(w, c.j * p.tpt + ri);
     const int v0 = c.nvis;
     const int a0 = min((v0 + 3) & ~3, p.W);
-    if ((int)threadIdx.x < a0 - v0)
-      row[v0 + threadIdx.x] = finish(p, w.L, start, v0 + threadIdx.x, false, 0.f);
-    for (int cc = a0 + 4 * (int)threadIdx.x; cc < p.W; cc += 4 * 256) {
+    if (tix < a0 - v0)
+      row[v0 + tix] = finish(p, w.L, start, v0 + tix, false, 0.f);
+    for (int cc = a0 + 4 * tix; cc < p.W; cc += 4 * nthr) {
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, start, cc + e, false, 0.f);
@@ -420,30 +476,7 @@ void decode_kernel(Params p) {
     }
   };
   auto fill_pass = [&]() {
-    if constexpr (!BIG) {
-      for (int it = wi; it < ntile * kDecodeRows; it += gu) {
-        const int k = it / kDecodeRows;
-        const int r = it - k * kDecodeRows;
-        Cursor c;
-        seek(p, first, k, true, c);
-        const Work w = tile_work(p, c, hk, hc);
-        const int ri = r / p.hpt;
-        const int rh = hc * p.hpt + (r - ri * p.hpt);
-        if (r >= p.hpt * p.tpt || ri >= w.ntok || rh >= p.g) continue;
-        float* const row = p.out + (((int64_t)hk * p.g + rh) * p.T + (w.t0 + ri)) * p.W;
-        const int start = local_anchor(p, w, c.j * p.tpt + ri);
-        const int v0 = c.nvis;
-        const int a0 = min((v0 + 3) & ~3, p.W);
-        if ((int)threadIdx.x < a0 - v0)
-          row[v0 + threadIdx.x] = finish(p, w.L, start, v0 + threadIdx.x, false, 0.f);
-        for (int cc = a0 + 4 * (int)threadIdx.x; cc < p.W; cc += 4 * 256) {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, start, cc + e, false, 0.f);
-          *reinterpret_cast<f32x4*>(row + cc) = v;
-        }
-      }
-    } else {
+    if constexpr (BIG) {
       const int nitems = ntile * kDecodeRows;
       const int per = (nitems + gu - 1) / gu;
       const int i0 = wi * per;
@@ -455,7 +488,7 @@ void decode_kernel(Params p) {
       for (int it = i0; it < i1; ++it) {
         const int k = it / kDecodeRows;
         for (; ck < k; ++ck) next_tile(p, c);
-        fill_item(c, it - k * kDecodeRows);
+        fill_item(c, it - k * kDecodeRows, (int)threadIdx.x, 256);
       }
     }
   };
@@ -465,22 +498,88 @@ void decode_kernel(Params p) {
   const int s0 = wi * per;
   const int s1 = min(ntask, s0 + per);
   int task = s0 + wave;
-  if (task >= s1) {
-    fill_pass();
-    return;
-  }
-
   Cursor c;
-  place(task, false, c);
+  // Batches of at most 64 requests: the waves take the slice's entries from
+  // an LDS counter, each its first one by its index, so that waves whose
+  // loads the memory system serves sooner take more blocks (with fixed
+  // shares, the workgroups of one CU finished 8-20 us apart: the CU's older
+  // waves are served first).  The next entry is taken as soon as a block's
+  // key loads are issued, so that the LDS round trip overlaps the wait for
+  // the keys.  Page indices come from a window of 64 consecutive entries of
+  // the slice held one per lane and read with readlane; a wave loads the
+  // window again only when it takes an entry past it.
+  auto take = [&](int which) -> int {
+    int r = 0;
+    if (l == 0) r = atomicAdd(&ctr[which], 1);
+    return __builtin_amdgcn_readfirstlane(r);
+  };
+  // Page index of entry wb + l (entries past the slice repeat its last):
+  // the entry belongs to the last request whose work starts at or before it,
+  // searched from the request of `from` (an entry at or before wb); its tile
+  // and block follow from the tiles' visible-block counts.
+  auto load_window = [&](int wb, const Cursor& from) -> int {
+    const int tau = min(wb + l, s1 - 1);
+    // lane r: first entry of request r; the requests after from.b that start
+    // inside the window are the only other candidates, and the last one
+    // starting at or before tau is found by halving steps over them
+    const int start = first.inc_tasks - first.tasks;
+    const int nreq = min(p.B, 64);
+    const int ncand = __popcll(__ballot(l > from.b && l < nreq && start <= wb + 63));
+    int b = from.b;
+    for (int step = ncand ? 1 << (31 - __builtin_clz(ncand)) : 0; step > 0; step >>= 1) {
+      const int r = b + step;
+      const int st = __shfl(start, min(r, 63));
+      if (r <= from.b + ncand && st <= tau) b = r;
+    }
+    const int ex = __shfl(start, b);
+    const int L = __shfl(first.kv, b), Lq = __shfl(first.lq, b);
+    int local = tau - ex;
+    int j = 0;
+    for (int nv = tile_blocks(p, L, Lq, 0); local >= nv; nv = tile_blocks(p, L, Lq, ++j))
+      local -= nv;
+    return p.block_table[(int64_t)b * p.MB + local];
+  };
+  int v = __builtin_amdgcn_readfirstlane(wave);  // entry of the slice (from s0)
+  int vnext = 0;
+  int wb = 0, pwin = 0;                          // page window: entries [s0 + wb, +64)
+  auto take_next = [&]() {
+    if constexpr (!BIG) {
+      vnext = take(0);
+      if (p.paged && vnext < s1 - s0 && vnext - wb >= 64) {
+        wb = vnext;
+        // (waited for here: it follows this block's key loads, which the
+        // block waits for anyway; left pending, the compiler would wait
+        // for every memory operation at the top of each block)
+        pwin = consumed(load_window(s0 + wb, c));
+      }
+    }
+  };
+  if constexpr (BIG) {
+    if (task >= s1) {
+      fill_pass();
+      return;
+    }
+    place(task, false, c);
+  } else if (v < s1 - s0) {
+    task = s0 + v;       // (wave-uniform to the compiler, as the cursor must be)
+    if (p.paged) {
+      Cursor c0;
+      place(s0, false, c0);
+      pwin = load_window(s0, c0);
+    }
+    place(task, false, c);
+    pwin = consumed(pwin);
+  }
   int cur_b = -1, cur_j = -1;
   Work w;
   i32x4 qv[4];
   int qs = 127;                  // MXFP4: the query scale of this lane's 32-element group
   int lim = -1, lim_lo = -1, start = 0;
-  // Paged keys: page indices of this wave's next blocks of the tile, lane k
-  // holding the k-th (blocks beta, beta + 4, ...), read with readlane; pk is
-  // the next lane to read (64: load again).  One load per tile instead of one
-  // per block keeps conditional memory reads out of the steady-state loop.
+  // Paged keys with the chunk table: page indices of this wave's next blocks
+  // of the tile, lane k holding the k-th (blocks beta, beta + 4, ...), read
+  // with readlane; pk is the next lane to read (64: load again).  One load
+  // per tile instead of one per block keeps conditional memory reads out of
+  // the steady-state loop.
   int pidx = 0, pk = 64;
   // A block's result is stored once the next block's key loads are issued:
   // storing it at the end of its own iteration made the compiler wait for
@@ -491,6 +590,15 @@ void decode_kernel(Params p) {
   bool row_ok = false;
   int ti = 0, hg = 0;
   for (;;) {
+    int dpage = 0;
+    if constexpr (!BIG) {
+      if (v >= s1 - s0) break;
+      if (task != s0 + v) {
+        advance_scan(p, first, c, s0 + v - task);
+        task = s0 + v;
+      }
+      if (p.paged) dpage = __builtin_amdgcn_readlane(pwin, v - wb);
+    }
     if (c.b != cur_b || c.j != cur_j) {
       // new tile: its query rows, windows and local_mask anchor
       cur_b = c.b;
@@ -503,7 +611,7 @@ void decode_kernel(Params p) {
       row_ok = (n < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
       lim = row_ok ? last_visible(p, w, i0 + ti) : -1;
       lim_lo = last_visible(p, w, i0);
-      start = local_anchor(p, w, i0 + ti);
+      start = anchor(w, i0 + ti);
 #pragma unroll
       for (int s = 0; s < 4; ++s) qv[s] = i32x4{0, 0, 0, 0};
       if (row_ok) {
@@ -532,13 +640,16 @@ void decode_kernel(Params p) {
     const int beta = c.beta;
     int64_t boff, soff;         // key byte offset, int8 scale element (MXFP4: byte) offset
     if (p.paged) {
-      if (pk == 64) {
-        const int bb = beta + 4 * l;
-        pidx = consumed(bb < c.nvis ? p.block_table[(int64_t)w.b * p.MB + bb] : 0);
-        pk = 0;
+      int page = dpage;
+      if constexpr (BIG) {
+        if (pk == 64) {
+          const int bb = beta + 4 * l;
+          pidx = consumed(bb < c.nvis ? p.block_table[(int64_t)w.b * p.MB + bb] : 0);
+          pk = 0;
+        }
+        page = __builtin_amdgcn_readlane(pidx, pk);
+        ++pk;
       }
-      const int page = __builtin_amdgcn_readlane(pidx, pk);
-      ++pk;
       boff = (int64_t)page * p.k_page_stride;
       soff = Kd::is_fp4 ? (int64_t)page * p.mx_page_stride + (int64_t)hk * p.mx_head_stride
                         : (int64_t)page * p.s_page_stride + (int64_t)hk * p.s_head_stride;
@@ -597,6 +708,7 @@ void decode_kernel(Params p) {
         return mm;
       };
       if (pend_ok) *pend_ptr = pend_val;
+      take_next();
       m = full ? score(std::false_type{}) : score(std::true_type{});
     } else if constexpr (Kd::is_f8 || Kd::is_i8) {
       // Key loads: instruction i reads rows 8i..8i+7 of the block whole (lane
@@ -669,6 +781,7 @@ void decode_kernel(Params p) {
         return mm;
       };
       if (pend_ok) *pend_ptr = pend_val;
+      take_next();
       m = full ? score(std::false_type{}) : score(std::true_type{});
     } else {
       // instruction i reads rows 4i..4i+3 whole (lane l: row 4i + l/16,
@@ -718,6 +831,7 @@ void decode_kernel(Params p) {
         return mm;
       };
       if (pend_ok) *pend_ptr = pend_val;
+      take_next();
       m = full ? score(std::false_type{}) : score(std::true_type{});
     }
     // the four k groups (lanes n + 16 G) hold disjoint key tokens of the
@@ -727,12 +841,32 @@ void decode_kernel(Params p) {
     pend_ptr = p.out + (((int64_t)hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W + beta;
     pend_val = finish(p, w.L, start, beta, true, m);
 
-    task += 4;
-    if (task >= s1) break;
-    advance(p, c, 4);
+    if constexpr (BIG) {
+      task += 4;
+      if (task >= s1) break;
+      advance(p, c, 4);
+    } else {
+      v = vnext;
+    }
   }
   if (pend_ok) *pend_ptr = pend_val;
-  fill_pass();
+  if constexpr (BIG) {
+    fill_pass();
+  } else {
+    // fill items of the workgroup's range, taken from the second counter by
+    // the waves as they run out of blocks; no memory reads
+    const int nitems = ntile * kDecodeRows;
+    const int fper = (nitems + gu - 1) / gu;
+    const int f0 = wi * fper;
+    const int f1 = min(nitems, f0 + fper);
+    for (int u = __builtin_amdgcn_readfirstlane(wave); f0 + u < f1; u = take(1)) {
+      const int it = f0 + u;
+      const int k = it / kDecodeRows;
+      Cursor cf;
+      seek(p, first, k, true, cf);
+      fill_item(cf, it - k * kDecodeRows, l, 64);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

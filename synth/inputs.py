@@ -576,7 +576,8 @@ def edge_cases() -> List[MsaCase]:
 def large_batch_cases() -> List[MsaCase]:
     """Batches of more than 64 requests (several 64-request chunks, the last
     one past a 256-chunk table), with short lengths so the oracle stays quick:
-    one-token decode, speculative and empty requests, paged and packed keys."""
+    one-token decode, speculative and empty requests, paged and packed keys;
+    and a 64-request batch whose workgroup slices run past one page window."""
     rng = np.random.default_rng(777)
     out = []
 
@@ -601,6 +602,15 @@ def large_batch_cases() -> List[MsaCase]:
                          q_lens=[int(x) for x in rng.choice([0, 1, 1, 1], size=16500)],
                          kv_lens=lens(16500, 0, 200), Hq=2, Hkv=1, qdtype="bf16", layout="TND",
                          sparse_mode=3, init_blocks=0, local_blocks=1))
+    # 64 requests (the at-most-64 kernel instance) with 128 heads per KV head:
+    # 16 units of eight head chunks share the chip, so each workgroup's slice
+    # holds ~90 (tile, block) entries over about three requests per 64 entries
+    # (its waves load the page window again past entry 64), and two-token
+    # requests have two tiles.
+    out.append(make_case("batch64_bbnd_bf16_g128", 7006,
+                         q_lens=[int(x) for x in rng.choice([1, 1, 2], size=64)],
+                         kv_lens=lens(64, 0, 6000), Hq=256, Hkv=2, qdtype="bf16", layout="BBND",
+                         sparse_mode=3, init_blocks=1, local_blocks=2))
     return out
 
 

@@ -109,7 +109,7 @@ def test_random_sweep_parity(idx, family, dev):
 
 
 LARGE_BATCH_NAMES = ["batch65_bbnd_bf16", "batch300_bnbd_i8_spec", "batch1000_tnd_f16",
-                     "batch200_bbnd_f16_perq", "batch16500_tnd_bf16"]
+                     "batch200_bbnd_f16_perq", "batch16500_tnd_bf16", "batch64_bbnd_bf16_g128"]
 _LARGE = []
 
 
@@ -126,7 +126,8 @@ def large_batch(idx):
 def test_large_batch_parity(idx, family, dev):
     # more than one 64-request chunk: the decode kernel's chunk table and
     # contiguous fill items, and the prefill request lookup, past 16384
-    # requests included
+    # requests included; and 64 requests whose decode workgroup slices run
+    # past one 64-entry page window, several requests to a window
     c = large_batch(idx)
     log(f"[gpu] large batch {c.name} family={family} {synth.case_summary(c)}")
     r = check(oracle_out(c), run_gpu(c, dev, family), tol_of(c))
