@@ -880,6 +880,17 @@ void decode_kernel(Params p) {
 // time, sixteen lanes to a row and one 16-byte store per lane, so an
 // instruction writes whole row segments; pieces that miss both windows skip
 // the per-column rule.
+// floor(r / d) for 0 <= r < 2^16 and 1 <= d < 2^16, without a division per
+// call: the high half of r * m with m = recip_small(d) = ceil(2^32 / d) (the
+// rounding error of m times r stays below 2^32, so the quotient never reaches
+// the next integer); m is 2^32 itself for d = 1.
+__device__ __forceinline__ uint64_t recip_small(int d) {
+  return (uint64_t)(0xFFFFFFFFu / (uint32_t)d) + 1;
+}
+__device__ __forceinline__ int div_small(int r, uint64_t m) {
+  return (int)(((uint64_t)(uint32_t)r * m) >> 32);
+}
+
 __device__ __forceinline__ void fill_tile_columns(const Params& p, const Work& w, int i0,
                                                   int c_lo, int c_hi) {
   const int np4 = (c_hi - c_lo) >> 2;
@@ -890,8 +901,10 @@ __device__ __forceinline__ void fill_tile_columns(const Params& p, const Work& w
   // the request's window end, read once (per query: from each row's position)
   const int req_anchor = (marks && !p.local_per_query) ? p.start_loc[w.b] : -1;
   const int nwaves = blockDim.x >> 6;
+  // (a division per row made the fill of a 48-block work item take ~30k cycles)
+  const uint64_t hinv = recip_small(p.hpt);
   for (int r = 4 * (threadIdx.x >> 6) + (l >> 4); r < nrows; r += 4 * nwaves) {
-    const int ti = r / p.hpt;
+    const int ti = div_small(r, hinv);
     const int hg = w.hc * p.hpt + (r - ti * p.hpt);
     if (hg >= p.g) continue;
     float* const row = p.out + (((int64_t)w.hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W;
@@ -971,10 +984,11 @@ void prefill_kernel(Params p) {
   int lim[NTW];
   i32x4 qv[NTW][8];
   int qsc[NTW][2];               // MXFP4: the query scale of each k step
+  const uint64_t hinv = recip_small(p.hpt);
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const int r = wave * 32 * NTW + nt * 32 + n;
-    const int ti = r / p.hpt;
+    const int ti = div_small(r, hinv);
     const int hg = w.hc * p.hpt + (r - ti * p.hpt);
     const bool ok = (r < p.hpt * p.tpt) && (ti < w.ntok) && (hg < p.g);
     lim[nt] = ok ? last_visible(p, w, i0 + ti) : -1;
@@ -1136,7 +1150,7 @@ void prefill_kernel(Params p) {
 #pragma unroll
   for (int u = 0; u < NOUT; ++u) {
     const int orow = wave * 32 * NTW + (G + 2 * u) * 32 + n;
-    const int oti = orow / p.hpt;
+    const int oti = div_small(orow, hinv);
     const int ohg = w.hc * p.hpt + (orow - oti * p.hpt);
     orow_ok[u] = G + 2 * u < NTW && orow < p.hpt * p.tpt && oti < w.ntok && ohg < p.g;
     orow_ptr[u] = p.out + (((int64_t)w.hk * p.g + ohg) * p.T + (w.t0 + oti)) * p.W;
