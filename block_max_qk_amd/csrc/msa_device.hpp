@@ -230,6 +230,8 @@ struct Work {
   int b, t0, ntok;             // request, first token, tokens in the tile
   int Lq, L;                   // query length and kv_len of the request
   int64_t koff;                // packed-key offset of the request (TND)
+  int sl;                      // start_loc of the request (prefill items; read
+                               // with the lookup, not with the per-query window)
 };
 
 __device__ __forceinline__ Work locate(const Params& p) {
@@ -256,10 +258,11 @@ __device__ __forceinline__ Work locate(const Params& p) {
   int64_t kacc = 0;
   for (int base = 0; base < p.B; base += 64) {
     const int b = base + l;
-    int lq = 0, kv = 0;
+    int lq = 0, kv = 0, sl = -1;
     if (b < p.B) {
       lq = p.cu_q[b + 1] - p.cu_q[b];
       kv = p.kv_len[b];
+      if (!p.local_per_query) sl = p.start_loc[b];
     }
     const int n = (lq + p.tpt - 1) / p.tpt;
     const int incl = wave_incl_scan(n);
@@ -279,6 +282,7 @@ __device__ __forceinline__ Work locate(const Params& p) {
       w.t0 = p.cu_q[w.b] + tin * p.tpt;
       w.ntok = min(p.tpt, w.Lq - tin * p.tpt);
       w.koff = kacc + kincl_s - kv_s;
+      w.sl = lane_at(sl, src);
       w.valid = 1;
       return w;
     }
@@ -305,6 +309,7 @@ __device__ __forceinline__ Work uniform_work(Work w) {
   w.Lq = u(w.Lq);
   w.L = u(w.L);
   w.koff = uniform64(w.koff);
+  w.sl = u(w.sl);
   return w;
 }
 

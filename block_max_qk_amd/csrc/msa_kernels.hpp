@@ -384,6 +384,7 @@ __device__ __forceinline__ Work tile_work(const Params& p, const Cursor& c, int 
   w.Lq = c.Lq;
   w.L = c.L;
   w.koff = c.koff;
+  w.sl = -1;                   // (decode reads start_loc through local_anchor)
   return w;
 }
 
@@ -873,13 +874,6 @@ void decode_kernel(Params p) {
 // prefill
 // ---------------------------------------------------------------------------
 
-// Columns [c_lo, c_hi) (multiples of 4) of every output row of a prefill
-// work item's tile where no block is scored: -inf, with the local_mask
-// constants where the init blocks or a row's local window fall (guide to
-// msa_index_score, sections 二 and 四).  Each wave takes four rows at a
-// time, sixteen lanes to a row and one 16-byte store per lane, so an
-// instruction writes whole row segments; pieces that miss both windows skip
-// the per-column rule.
 // floor(r / d) for 0 <= r < 2^16 and 1 <= d < 2^16, without a division per
 // call: the high half of r * m with m = recip_small(d) = ceil(2^32 / d) (the
 // rounding error of m times r stays below 2^32, so the quotient never reaches
@@ -891,34 +885,49 @@ __device__ __forceinline__ int div_small(int r, uint64_t m) {
   return (int)(((uint64_t)(uint32_t)r * m) >> 32);
 }
 
+// Columns [c_lo, c_hi) (multiples of 4, at most 64 of them) of every output
+// row of a prefill work item's tile (at most 512 rows) where no block is
+// scored: -inf, with the local_mask constants where the init blocks or a
+// row's local window fall (guide to msa_index_score, sections 二 and 四).
+// The workgroup walks the (row, 16-byte piece) pairs in order, one store per
+// lane, so that an instruction writes consecutive pieces of consecutive rows
+// and every lane stores.  With the window at start_loc whether any piece can
+// hold a constant is known for the whole item; otherwise per row.  (A loop
+// over four rows per wave step, sixteen lanes to a row, with the row's
+// division and window recomputed per step, made the items that only write
+// fill take ~6% of the varlen MXFP4 prefill.)
 __device__ __forceinline__ void fill_tile_columns(const Params& p, const Work& w, int i0,
                                                   int c_lo, int c_hi) {
   const int np4 = (c_hi - c_lo) >> 2;
   if (np4 <= 0) return;
-  const int l = lane_id();
   const int nrows = p.hpt * w.ntok;
   const bool marks = w.L > 0 && (p.init_blocks > 0 || p.local_blocks > 0);
-  // the request's window end, read once (per query: from each row's position)
-  const int req_anchor = (marks && !p.local_per_query) ? p.start_loc[w.b] : -1;
-  const int nwaves = blockDim.x >> 6;
-  // (a division per row made the fill of a 48-block work item take ~30k cycles)
+  // the request's window end (per query: from each row's position)
+  const int req_anchor = (marks && !p.local_per_query) ? w.sl : -1;
+  const bool any_mark =
+      marks && (p.local_per_query || c_lo < p.init_blocks ||
+                (c_hi > max(0, req_anchor + 1 - p.local_blocks) && c_lo <= req_anchor));
+  const uint64_t pinv = recip_small(np4);
   const uint64_t hinv = recip_small(p.hpt);
-  for (int r = 4 * (threadIdx.x >> 6) + (l >> 4); r < nrows; r += 4 * nwaves) {
+  float* const base = p.out + (((int64_t)w.hk * p.g + w.hc * p.hpt) * p.T + w.t0) * p.W;
+  const int n = nrows * np4;           // below 2^16: 512 rows x 16 pieces at most
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int r = div_small(e, pinv);
+    const int q = e - r * np4;
     const int ti = div_small(r, hinv);
-    const int hg = w.hc * p.hpt + (r - ti * p.hpt);
-    if (hg >= p.g) continue;
-    float* const row = p.out + (((int64_t)w.hk * p.g + hg) * p.T + (w.t0 + ti)) * p.W;
-    const int anchor = !marks ? -1 : p.local_per_query ? query_anchor(w, i0 + ti) : req_anchor;
-    const int lo = max(0, anchor + 1 - p.local_blocks);
-    for (int q = l & 15; q < np4; q += 16) {
-      const int beta = c_lo + 4 * q;
-      f32x4 v = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-      if (marks && (beta < p.init_blocks || (beta + 3 >= lo && beta <= anchor))) {
+    const int hl = r - ti * p.hpt;     // head within the tile's head chunk
+    if (w.hc * p.hpt + hl >= p.g) continue;
+    const int beta = c_lo + 4 * q;
+    f32x4 v = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+    if (any_mark) {
+      const int anchor = p.local_per_query ? query_anchor(w, i0 + ti) : req_anchor;
+      const int lo = max(0, anchor + 1 - p.local_blocks);
+      if (beta < p.init_blocks || (beta + 3 >= lo && beta <= anchor)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = finish(p, w.L, anchor, beta + e, false, 0.f);
+        for (int k = 0; k < 4; ++k) v[k] = finish(p, w.L, anchor, beta + k, false, 0.f);
       }
-      *reinterpret_cast<f32x4*>(row + beta) = v;
     }
+    *reinterpret_cast<f32x4*>(base + ((int64_t)hl * p.T + ti) * p.W + beta) = v;
   }
 }
 
@@ -1154,7 +1163,7 @@ void prefill_kernel(Params p) {
     const int ohg = w.hc * p.hpt + (orow - oti * p.hpt);
     orow_ok[u] = G + 2 * u < NTW && orow < p.hpt * p.tpt && oti < w.ntok && ohg < p.g;
     orow_ptr[u] = p.out + (((int64_t)w.hk * p.g + ohg) * p.T + (w.t0 + oti)) * p.W;
-    oanc[u] = local_anchor(p, w, i0 + oti);
+    oanc[u] = p.local_per_query ? query_anchor(w, i0 + oti) : w.sl;
   }
 
   const int nst = busy ? (vend - w.c0) * SPB : 0;   // stages of this work item
@@ -1362,6 +1371,19 @@ void prefill_kernel(Params p) {
               tile_max(acc2[(mt - 1) & 1], mt - 1, NTW / 2, NTW);
           }
           if (i == NFR - 1) tile_max(ac, mt, 0, NTW);
+          if constexpr (!MASKED) {
+            // one MFMA, then four of the previous tile's maxima (v_max3),
+            // so that a wave's vector work issues while its own MFMAs run;
+            // left to the compiler the four MFMAs went out back to back and
+            // the maxima after them
+            if (mt > 0) {
+#pragma unroll
+              for (int k = 0; k < NTW; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+              }
+            }
+          }
         } else if constexpr (Kd::is_f8) {
           if (q & 1) {
             const int s = q >> 1;
