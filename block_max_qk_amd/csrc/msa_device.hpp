@@ -171,6 +171,14 @@ __device__ __forceinline__ void buffer_copy16_lds(__amdgpu_buffer_rsrc_t rs, uin
                                            voff, 0, 0, 0);
 }
 
+// One 4-byte word per lane from a raw buffer straight into LDS: lane l's
+// word lands at lds + 4 l.
+__device__ __forceinline__ void buffer_copy4_lds(__amdgpu_buffer_rsrc_t rs, uint8_t* lds,
+                                                 uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ i32x4 ld16(const uint8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }

@@ -955,17 +955,13 @@ void prefill_kernel(Params p) {
   __shared__ float scl[2][kP];
   // MXFP4: the scale words of every block of the work item, lane-major:
   // [block][n][mt] holds token 32 mt + n's word, so that lane (n, G) reads its
-  // block's four M tiles with one 16-byte LDS read.  Staged once, before the
+  // block's four M tiles with one 16-byte LDS read.  Copied once, before the
   // block loop, so that the loop issues no register loads: with register
   // loads in flight beside the LDS copies (and stores) the compiler waits for
   // every memory operation before using them.
   constexpr int CHUNK = prefill_chunk(KK);     // blocks per work item at most
   static_assert(CHUNK <= 64, "page indices are held one per lane");
   __shared__ __attribute__((aligned(16))) uint32_t kmx[Kd::is_fp4 ? CHUNK : 1][32][4];
-  // MXFP4: each wave's copy of the work item's page indices, read per lane
-  // while staging the scales (readlane of the index register made the
-  // compiler wait for every load in flight before each one)
-  __shared__ int32_t kpg[Kd::is_fp4 ? kPrefillWaves : 1][CHUNK];
 
   const Work w = uniform_work(locate(p));
   if (!w.valid) return;
@@ -1088,34 +1084,29 @@ void prefill_kernel(Params p) {
     const int X = wave * NI + q;
     buffer_copy16_lds(rs, kl + slot * SBYTES + X * 1024, (uint32_t)(off * p.k_row_stride) + cof[q]);
   };
-  // MXFP4: stage the scale words of the work item's nblk blocks into kmx
-  // (rows past kv_len read row 0; their scores are masked).  Entry e = tid +
-  // 256 i is token e % 128 of block e / 128 (the same block across a wave);
-  // all loads are issued before the first LDS write (entries past the last
-  // block re-read it and are not written).
+  // MXFP4: the scale words of the work item's nblk blocks, copied straight
+  // into kmx: two copies per block, wave w taking blocks w, w + 4, ...; lane
+  // l of copy k loads token 32 (l & 3) + 16 k + (l >> 2), whose word lands at
+  // slot 64 k + l = 4 n + mt of the block's [n][mt] area.  The buffer ends at
+  // the block's last row below kv_len, so rows past it read zeros (their
+  // scores are masked).  (Register loads and LDS stores took 24 loads per
+  // lane before the first block: 2-4% of the MXFP4 prefill.)
   auto stage_scales = [&](int nblk) {
-    constexpr int NE = CHUNK * kP / 256;
-    if (p.paged && l < CHUNK) kpg[wave][l] = pidx;
-    wave_lds_sync();
-    uint32_t sv4[NE];
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = tid + 256 * i;
-      const int bi = min(e / kP, nblk - 1);
-      const int jj = e % kP;
+    const uint32_t tof = (uint32_t)((32 * (l & 3) + (l >> 2)) * p.mx_row_stride);
+    const uint32_t tof16 = tof + 16u * (uint32_t)p.mx_row_stride;
+    for (int bi = wave; bi < nblk; bi += kPrefillWaves) {
       const int beta = w.c0 + bi;
       const int64_t base =
-          (p.paged ? (int64_t)kpg[wave][bi] * p.mx_page_stride
+          (p.paged ? (int64_t)__builtin_amdgcn_readlane(pidx, bi) * p.mx_page_stride
                    : (w.koff + (int64_t)beta * kP) * p.mx_row_stride) +
           (int64_t)w.hk * p.mx_head_stride;
       const int nvalid = min(kP, w.L - beta * kP);
-      const int src = jj < nvalid ? jj : 0;
-      sv4[i] = *reinterpret_cast<const uint32_t*>(p.k_mx + base + (int64_t)src * p.mx_row_stride);
-    }
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int e = tid + 256 * i;
-      if (e < nblk * kP) kmx[e / kP][e & 31][(e % kP) >> 5] = sv4[i];
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(p.k_mx + uniform64(base)), 0,
+          (nvalid - 1) * p.mx_row_stride + 4, kBufferWord3);
+      uint8_t* const dst = reinterpret_cast<uint8_t*>(kmx) + bi * 512;
+      buffer_copy4_lds(rs, dst, tof);
+      buffer_copy4_lds(rs, dst + 256, tof16);
     }
   };
   auto stage_async = [&](int sg, int slot, int64_t kbytes) {
@@ -1170,13 +1161,13 @@ void prefill_kernel(Params p) {
   if constexpr (ASYNC) {
     // the first block's page index is read before any copy is in flight
     const int64_t kb0 = nst > 0 ? block_bytes(w.c0) : 0;
+    if constexpr (Kd::is_fp4) {
+      if (nst > 0) stage_scales(vend - w.c0);
+    }
 #pragma unroll
     for (int sg = 0; sg < RING - 1; ++sg)
       if (sg < nst) stage_async(sg, sg, sg < SPB ? kb0 : block_bytes(w.c0 + sg / SPB));
     // (the loop's first barrier makes every wave's writes visible)
-    if constexpr (Kd::is_fp4) {
-      if (nst > 0) stage_scales(vend - w.c0);
-    }
   } else {
     if (nst > 0) {
       gload_i8(w.c0);
