@@ -435,6 +435,16 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp4(i32x4 a, i32x4 b, f32x16 c, i
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
 }
 
+// The same with the scale bytes chosen by the instruction: byte SA of sa
+// and byte SB of sb.
+template <int SA, int SB>
+__device__ __forceinline__ f32x16 mfma32x32x64_fp4_sel(i32x4 a, i32x4 b, f32x16 c, int sa,
+                                                       int sb) {
+  const i32x8 a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const i32x8 b8 = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SA, sa, SB, sb);
+}
+
 // The 16x16x128 form: lane l covers row l % 16 and the 32 elements
 // 32 (l / 16) + [0, 32) of the 128-deep product (16 bytes), scale byte 0 of
 // sa / sb; lane l's result is column l % 16, rows 4 (l / 16) + [0, 4).

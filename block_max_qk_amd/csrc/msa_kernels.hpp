@@ -938,18 +938,19 @@ void prefill_kernel(Params p) {
   constexpr int NTW = prefill_ntw(KK);
   // Key blocks pass through an LDS ring of stages.  16-bit keys: stages of 64
   // tokens (16 KB), three deep, so a stage's copy has two compute periods to
-  // land; fp8: whole 128-token blocks (16 KB), two deep; MXFP4: whole blocks
-  // (8 KB; their scales are staged for the whole work item up front), three
+  // land; fp8: whole 128-token blocks (16 KB), two deep; MXFP4: two blocks
+  // (16 KB; their scales are staged for the whole work item up front), two
   // deep; int8 (widened to fp16 through registers): whole blocks (32 KB), two
-  // deep.  All of it fits three workgroups per CU (two for int8).
+  // deep.  All of it fits two workgroups per CU, three for fp8.
   constexpr int RB = Kd::is_fp4 ? 64 : (Kd::is_f8 ? 128 : 256);   // LDS bytes per key token
   constexpr bool ASYNC = !Kd::is_i8;           // copy HBM/L2 -> LDS directly
-  constexpr int ST = (ASYNC && RB == 256) ? 64 : kP;   // tokens per stage
-  constexpr int SPB = kP / ST;                 // stages per block
-  constexpr int RING = (SPB == 2 || Kd::is_fp4) ? 3 : 2;
+  constexpr int BPS = Kd::is_fp4 ? 2 : 1;      // blocks per stage
+  constexpr int ST = Kd::is_fp4 ? BPS * kP : (ASYNC && RB == 256) ? 64 : kP;   // tokens per stage
+  constexpr int SPB = Kd::is_fp4 ? 1 : kP / ST;   // stages per block (MXFP4: see its loop)
+  constexpr int RING = SPB == 2 ? 3 : 2;
   constexpr int SBYTES = ST * RB;
   constexpr int NI = SBYTES / 1024 / 4;        // copy instructions per wave per stage
-  static_assert(!ASYNC || RING == 2 || NI == (Kd::is_fp4 ? 2 : 4),
+  static_assert(!ASYNC || RING == 2 || NI == 4,
                 "the three-deep ring's wait counts assume these copies per wave per stage");
   __shared__ __attribute__((aligned(16))) uint8_t kl[RING * SBYTES];
   __shared__ float scl[2][kP];
@@ -988,7 +989,9 @@ void prefill_kernel(Params p) {
 
   int lim[NTW];
   i32x4 qv[NTW][8];
-  int qsc[NTW][2];               // MXFP4: the query scale of each k step
+  // MXFP4: this lane's query scales, byte s for k step s (the MFMA selects
+  // the byte)
+  int qsw[NTW];
   const uint64_t hinv = recip_small(p.hpt);
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
@@ -999,7 +1002,7 @@ void prefill_kernel(Params p) {
     lim[nt] = ok ? last_visible(p, w, i0 + ti) : -1;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qv[nt][s] = i32x4{0, 0, 0, 0};
-    qsc[nt][0] = qsc[nt][1] = 127;
+    qsw[nt] = 0x7F7F;
     if (ok && busy) {
       const int64_t qrow = (int64_t)(w.t0 + ti) * p.Hq + (w.hk * p.g + hg);
       const uint8_t* qr = p.q + qrow * Kd::q_row;
@@ -1007,10 +1010,8 @@ void prefill_kernel(Params p) {
         // k step s (64 deep) of group G: bytes [32s + 16G, +16), scale 2s + G
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(p.q_mx + qrow * (kD / 32));
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          qv[nt][s] = ld16(qr + 32 * s + 16 * G);
-          qsc[nt][s] = (sw >> (8 * (2 * s + G))) & 255;
-        }
+        for (int s = 0; s < 2; ++s) qv[nt][s] = ld16(qr + 32 * s + 16 * G);
+        qsw[nt] = (int)(((sw >> (8 * G)) & 0xFF) | (((sw >> (8 * (2 + G))) & 0xFF) << 8));
       } else if constexpr (Kd::is_f8) {
         // k step s (64 deep) of group G: bytes [64s + 32G, +32)
 #pragma unroll
@@ -1059,30 +1060,40 @@ void prefill_kernel(Params p) {
   // This lane's byte offset within a stage for each of its wave's copy
   // instructions (token jl of the stage, swizzled 16-byte chunk c), computed
   // once per work item.
-  constexpr int NCOF = ASYNC ? NI : 1;
+  // (MXFP4: the copies of a wave are 16 rows apart and the swizzle does not
+  // see those row bits, so one offset serves all four)
+  constexpr int NCOF = Kd::is_fp4 ? 1 : ASYNC ? NI : 1;
   uint32_t cof[NCOF];
 #pragma unroll
   for (int q = 0; q < NCOF; ++q) {
+    // (MXFP4: token jl of the stage's two blocks, row jl mod 128 of its block)
     const int jl = (wave * NI + q) * RPI + l / (RB / 16);
+    const int jb = Kd::is_fp4 ? (jl & (kP - 1)) : jl;
     const int c = (l % (RB / 16)) ^
-                  (RB == 256 ? (jl & 15) : RB == 128 ? ((jl >> 1) & 7) : ((jl >> 2) & 3));
-    cof[q] = (uint32_t)(jl * p.k_row_stride + 16 * c);
+                  (RB == 256 ? (jb & 15) : RB == 128 ? ((jb >> 1) & 7) : ((jb >> 2) & 3));
+    cof[q] = (uint32_t)(jb * p.k_row_stride + 16 * c);
   }
   // Copy instruction q of stage sg, through a raw buffer over the block's
   // rows below kv_len (its size nvalid rows): lanes of rows at or past
   // kv_len read zeros, which only blocks that take the masked path contain.
   // No per-copy branch or clamp; the block base and LDS destination are
   // scalar values.
+  // (MXFP4: a stage is blocks c0 + 2 sg and c0 + 2 sg + 1; waves 0-1 copy
+  // the first, 2-3 the second, from the block base `kbytes` of their own
+  // block, which may lie past the request's last block: then nothing is read)
   auto stage_copy = [&](int q, int sg, int slot, int64_t kbytes) {
-    const int beta = w.c0 + sg / SPB;
-    const int off = (sg % SPB) * ST;
+    const int beta = Kd::is_fp4 ? w.c0 + BPS * sg + (wave >> 1) : w.c0 + sg / SPB;
+    const int off = Kd::is_fp4 ? 0 : (sg % SPB) * ST;
     // offsets within a block fit 32 bits (checked on the host)
     const uint8_t* kb = p.k + uniform64(kbytes + (int64_t)w.hk * p.k_head_stride);
-    const int nvalid = min(kP, w.L - beta * kP);
+    // (a scalar: computed in vector registers, the buffer descriptor made the
+    // compiler wrap each copy in a loop over lanes)
+    const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(kP, w.L - beta * kP)));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(kb), 0, nvalid * p.k_row_stride, kBufferWord3);
     const int X = wave * NI + q;
-    buffer_copy16_lds(rs, kl + slot * SBYTES + X * 1024, (uint32_t)(off * p.k_row_stride) + cof[q]);
+    const uint32_t co = Kd::is_fp4 ? cof[0] + (uint32_t)(q * RPI * p.k_row_stride) : cof[q];
+    buffer_copy16_lds(rs, kl + slot * SBYTES + X * 1024, (uint32_t)(off * p.k_row_stride) + co);
   };
   // MXFP4: the scale words of the work item's nblk blocks, copied straight
   // into kmx: two copies per block, wave w taking blocks w, w + 4, ...; lane
@@ -1160,7 +1171,8 @@ void prefill_kernel(Params p) {
   const int nst = busy ? (vend - w.c0) * SPB : 0;   // stages of this work item
   if constexpr (ASYNC) {
     // the first block's page index is read before any copy is in flight
-    const int64_t kb0 = nst > 0 ? block_bytes(w.c0) : 0;
+    // (MXFP4: the wave's own block of the first stage)
+    const int64_t kb0 = nst > 0 ? block_bytes(w.c0 + (Kd::is_fp4 ? (wave >> 1) : 0)) : 0;
     if constexpr (Kd::is_fp4) {
       if (nst > 0) stage_scales(vend - w.c0);
     }
@@ -1221,6 +1233,142 @@ void prefill_kernel(Params p) {
       }
     }
   };
+  if constexpr (Kd::is_fp4) {
+    // Stages of two blocks, A = c0 + 2 sg and B = A + 1 (B may lie past the
+    // item's last block; its results are then dropped).  The 32-token M
+    // tiles of the two blocks alternate (A0 B0 A1 B1 ...), A's on accumulator
+    // set 0 and B's on set 1, and a tile's maxima are taken while the next
+    // tile's MFMAs run, so that only B's last tile ends the stage with vector
+    // work waiting on its own MFMAs; one barrier per two blocks.
+    const int nst2 = (vend - w.c0 + 1) >> 1;
+    f32x4 run2[2];
+    f32x16 acc2[2][NTW];
+    auto finalize2 = [&](int bis, int bb) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) run2[bis][nt] = max_xor32(run2[bis][nt]);
+      const int kk = (bb - w.c0) % RG;
+#pragma unroll
+      for (int u = 0; u < NOUT; ++u)
+        resl[wave][u][kk][l] = (G && 2 * u + 1 < NTW) ? run2[bis][2 * u + 1] : run2[bis][2 * u];
+      if (kk == RG - 1 || bb == vend - 1) pend = bb - kk;
+    };
+    for (int sg = 0; sg < nst2; ++sg) {
+      const int slot = sg & 1;
+      const int beta0 = w.c0 + 2 * sg;
+      const bool hasB = beta0 + 1 < vend;
+      // this stage has landed (every wave's copies) and every wave is done
+      // with the slot the copy below refills
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (pend >= 0) {
+        flush(pend);
+        pend = -1;
+      }
+      const int csg = sg + 1;
+      const bool copy_next = csg < nst2;
+      const int64_t ckb = copy_next ? block_bytes(w.c0 + 2 * csg + (wave >> 1)) : 0;
+      const uint8_t* kc = kl + slot * SBYTES;
+#pragma unroll
+      for (int bis = 0; bis < 2; ++bis) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) run2[bis][nt] = -__builtin_inff();
+      }
+      const bool unmasked = (hasB ? beta0 + 1 : beta0) * kP + kP - 1 <= lim_lo;
+      auto stage = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        constexpr int NFR = 16;      // (M tile, block, k step), k step fastest
+        // fragments read ahead: four (one more spills the masked variant,
+        // whose mask tests hold more registers; it reads two ahead)
+        constexpr int LEAD = MASKED ? 2 : 4;
+        auto frag = [&](int i) -> i32x4 {
+          const int mt = i >> 2, bis = (i >> 1) & 1, q = i & 1;
+          const int jj = mt * 32 + n;
+          const int c = 2 * q + G;   // bytes [32q + 16G, +16) of the token
+          return *reinterpret_cast<const i32x4*>(kc + bis * (kP * RB) + jj * RB +
+                                                  ((c ^ ((jj >> 2) & 3)) << 4));
+        };
+        i32x4 f[NFR];
+#pragma unroll
+        for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
+        // the two blocks' scale words, token 32 mt + n in word mt, shifted
+        // so that byte 2q is this lane's group 2q + G (the MFMA selects it)
+        uint32_t ksw[2][4];
+#pragma unroll
+        for (int bis = 0; bis < 2; ++bis) {
+          const uint4 kw =
+              *reinterpret_cast<const uint4*>(&kmx[min(beta0 + bis - w.c0, CHUNK - 1)][n][0]);
+          const int sh = 8 * G;
+          ksw[bis][0] = kw.x >> sh;
+          ksw[bis][1] = kw.y >> sh;
+          ksw[bis][2] = kw.z >> sh;
+          ksw[bis][3] = kw.w >> sh;
+        }
+        // a[nt][r] is key token 32 mt + 8 (r / 4) + 4 G + r % 4 of the block
+        // for row n of N tile nt; masked: kept iff at most the row's last
+        // visible token, i.e. 8 (r / 4) + r % 4 <= lim - (block start + 32 mt
+        // + 4 G)
+        auto tile_max = [&](const f32x16 (&a)[NTW], int bis, int mt, int nt0, int nt1) {
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) {
+            if (nt < nt0 || nt >= nt1) continue;
+            const int vis = MASKED ? lim[nt] - ((beta0 + bis) * kP + mt * 32 + 4 * G) : 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float v = a[nt][r];
+              if constexpr (MASKED) v = (8 * (r >> 2) + (r & 3) <= vis) ? v : -__builtin_inff();
+              run2[bis][nt] = fmaxf(run2[bis][nt], v);
+            }
+          }
+        };
+#pragma unroll
+        for (int i = 0; i < NFR; ++i) {
+          if (copy_next && i == 0) {
+#pragma unroll
+            for (int q = 0; q < NI; ++q) stage_copy(q, csg, csg & 1, ckb);
+          }
+          if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
+          const int mt = i >> 2, bis = (i >> 1) & 1, q = i & 1, k = i >> 1;
+          f32x16 (&ac)[NTW] = acc2[bis];
+          if (q == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) ac[nt] = f32x16{};
+          }
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            ac[nt] = q == 0 ? mfma32x32x64_fp4_sel<0, 0>(f[i], qv[nt][0], ac[nt], ksw[bis][mt], qsw[nt])
+                            : mfma32x32x64_fp4_sel<2, 1>(f[i], qv[nt][1], ac[nt], ksw[bis][mt], qsw[nt]);
+          if (k > 0) {
+            // tile k - 1 (the other block's), half of its N tiles per fragment
+            const int pb = (k - 1) & 1, pm = (k - 1) >> 1;
+            if (q == 0)
+              tile_max(acc2[pb], pb, pm, 0, NTW / 2);
+            else
+              tile_max(acc2[pb], pb, pm, NTW / 2, NTW);
+          }
+          if (i == NFR - 1) tile_max(ac, 1, 3, 0, NTW);
+          if constexpr (!MASKED) {
+            // one MFMA, then four of the previous tile's maxima (v_max3),
+            // so that a wave's vector work issues while its own MFMAs run
+            if (k > 0) {
+#pragma unroll
+              for (int kk = 0; kk < NTW; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+              }
+            }
+          }
+          // keep this shape: one fragment read, its MFMAs, (an epilogue)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (unmasked)
+        stage(std::false_type{});
+      else
+        stage(std::true_type{});
+      finalize2(0, beta0);
+      if (hasB) finalize2(1, beta0 + 1);
+    }
+    if (pend >= 0) flush(pend);
+  } else {
   for (int sg = 0; sg < nst; ++sg) {
     const int slot = sg % RING;
     const int beta = w.c0 + sg / SPB;
@@ -1270,18 +1418,13 @@ void prefill_kernel(Params p) {
       // of a 32-byte operand.  Fragment i + LEAD is read from LDS while
       // fragment i feeds the MFMAs, which hides the LDS latency with only
       // LEAD + 1 fragments live.
-      constexpr int PER_MT = Kd::is_fp4 ? 2 : Kd::is_f8 ? 4 : 8;   // fragments per M tile
+      constexpr int PER_MT = Kd::is_f8 ? 4 : 8;   // fragments per M tile
       constexpr int NFR = (ST / 32) * PER_MT;
-      // (MXFP4: 4 measured 1% faster than 2, and the same as 6 or 8)
-      constexpr int LEAD = (Kd::is_fp4 || Kd::is_f8) ? 4 : (NTW >= 3 ? 1 : 2);
+      constexpr int LEAD = Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
       auto frag = [&](int i) -> i32x4 {
         const int mt = i / PER_MT, q = i % PER_MT;
         const int jj = mt * 32 + n;
-        if constexpr (Kd::is_fp4) {
-          // q = k step s: bytes [32s + 16G, +16) of the token, chunk 2s + G
-          const int c = 2 * q + G;
-          return *reinterpret_cast<const i32x4*>(kc + jj * 64 + ((c ^ ((jj >> 2) & 3)) << 4));
-        } else if constexpr (Kd::is_f8) {
+        if constexpr (Kd::is_f8) {
           // q = 2*s + half: bytes [64s + 32G + 16*half, +16) of the token
           const int c = 4 * (q >> 1) + 2 * G + (q & 1);
           return *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ ((jj >> 1) & 7)) << 4));
@@ -1294,37 +1437,6 @@ void prefill_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
       f32x16 acc[NTW];
-      // MXFP4: two accumulator sets, M tiles alternating; an M tile's
-      // maxima are taken while the next tile's MFMAs run (half of its N
-      // tiles after each of the next tile's two fragments), so that each
-      // wave's vector work overlaps its own matrix work
-      static_assert(!Kd::is_fp4 || PER_MT == 2, "MXFP4 epilogue halves assume two fragments per M tile");
-      f32x16 acc2[Kd::is_fp4 ? 2 : 1][Kd::is_fp4 ? NTW : 1];
-      auto tile_max = [&](const f32x16 (&a)[Kd::is_fp4 ? NTW : 1], int mt, int nt0, int nt1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jr = off + mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
-#pragma unroll
-          for (int nt = 0; nt < (Kd::is_fp4 ? NTW : 1); ++nt) {
-            if (nt < nt0 || nt >= nt1) continue;
-            float v = a[nt][r];
-            if constexpr (MASKED) {
-              const int j = beta * kP + jr;
-              v = (j <= lim[nt]) ? v : -__builtin_inff();
-            }
-            run[nt] = fmaxf(run[nt], v);
-          }
-        }
-      };
-      // MXFP4: this block's scale words, token 32 mt + n in word mt
-      uint32_t ksw[Kd::is_fp4 ? 4 : 1];
-      if constexpr (Kd::is_fp4) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(&kmx[beta - w.c0][n][0]);
-        ksw[0] = kw.x;
-        ksw[1] = kw.y;
-        ksw[2] = kw.z;
-        ksw[3] = kw.w;
-      }
 #pragma unroll
       for (int i = 0; i < NFR; ++i) {
         if constexpr (ASYNC) {
@@ -1340,42 +1452,11 @@ void prefill_kernel(Params p) {
         }
         if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
         const int mt = i / PER_MT, q = i % PER_MT;
-        if (!Kd::is_fp4 && q == 0) {
+        if (q == 0) {
 #pragma unroll
           for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x16{};
         }
-        if constexpr (Kd::is_fp4) {
-          // byte 2q + G of the token's scale word is this lane's group
-          const int sa = (ksw[mt] >> (8 * (2 * q + G))) & 255;
-          f32x16 (&ac)[NTW] = acc2[mt & 1];
-          if (q == 0) {
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) ac[nt] = f32x16{};
-          }
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-            ac[nt] = mfma32x32x64_fp4(f[i], qv[nt][q], ac[nt], sa, qsc[nt][q]);
-          if (mt > 0) {
-            if (q == 0)
-              tile_max(acc2[(mt - 1) & 1], mt - 1, 0, NTW / 2);
-            else
-              tile_max(acc2[(mt - 1) & 1], mt - 1, NTW / 2, NTW);
-          }
-          if (i == NFR - 1) tile_max(ac, mt, 0, NTW);
-          if constexpr (!MASKED) {
-            // one MFMA, then four of the previous tile's maxima (v_max3),
-            // so that a wave's vector work issues while its own MFMAs run;
-            // left to the compiler the four MFMAs went out back to back and
-            // the maxima after them
-            if (mt > 0) {
-#pragma unroll
-              for (int k = 0; k < NTW; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-              }
-            }
-          }
-        } else if constexpr (Kd::is_f8) {
+        if constexpr (Kd::is_f8) {
           if (q & 1) {
             const int s = q >> 1;
             const i32x8 a = cat(f[i - 1], f[i]);
@@ -1388,7 +1469,7 @@ void prefill_kernel(Params p) {
           for (int nt = 0; nt < NTW; ++nt)
             acc[nt] = mfma32x32x16<Kd::mfma_kind>(f[i], qv[nt][q], acc[nt]);
         }
-        if (!Kd::is_fp4 && q == PER_MT - 1) {
+        if (q == PER_MT - 1) {
           // acc[nt][r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -1425,12 +1506,8 @@ void prefill_kernel(Params p) {
 #pragma unroll
       for (int u = 0; u < NOUT; ++u) {
         const float v = (G && 2 * u + 1 < NTW) ? run[2 * u + 1] : run[2 * u];
-        if constexpr (LDS_RES) {
-          resl[wave][u][kk][l] = v;
-        } else {
 #pragma unroll
-          for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
-        }
+        for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
       }
       if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
     }
@@ -1440,6 +1517,7 @@ void prefill_kernel(Params p) {
   }
 
   if (pend >= 0) flush(pend);
+  }
   // columns of the work item past the last group: -inf and local_mask
   fill_tile_columns(p, w, i0, w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG, w.c1);
 }
