@@ -1209,29 +1209,43 @@ void prefill_kernel(Params p) {
   __shared__ float resl[LDS_RES ? kPrefillWaves : 1][LDS_RES ? NOUT : 1][LDS_RES ? RG : 1][64];
   float resv[NOUT][LDS_RES ? 1 : RG];
   int pend = -1;                 // first block of a group waiting to be written
+  // Whether a column of the group can hold a local_mask constant is, with
+  // the window at start_loc, the same for every row of the item: groups that
+  // miss both windows skip the per-column rule.
+  const bool marks = w.L > 0 && (p.init_blocks > 0 || p.local_blocks > 0);
   auto flush = [&](int g0) {
+    auto write = [&](auto rule) {
 #pragma unroll
-    for (int u = 0; u < NOUT; ++u) {
-      if (orow_ok[u]) {
+      for (int u = 0; u < NOUT; ++u) {
+        if (orow_ok[u]) {
 #pragma unroll
-        for (int c = 0; c < RG; c += 4) {
-          if (g0 + c < w.c1) {
-            f32x4 v;
+          for (int c = 0; c < RG; c += 4) {
+            if (g0 + c < w.c1) {
+              f32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int beta = g0 + c + e;
-              float r;
-              if constexpr (LDS_RES)
-                r = resl[wave][u][c + e][l];
-              else
-                r = resv[u][c + e];
-              v[e] = finish(p, w.L, oanc[u], beta, beta < vend, r);
+              for (int e = 0; e < 4; ++e) {
+                const int beta = g0 + c + e;
+                float r;
+                if constexpr (LDS_RES)
+                  r = resl[wave][u][c + e][l];
+                else
+                  r = resv[u][c + e];
+                if constexpr (decltype(rule)::value)
+                  v[e] = finish(p, w.L, oanc[u], beta, beta < vend, r);
+                else
+                  v[e] = beta < vend ? r : -__builtin_inff();
+              }
+              *reinterpret_cast<f32x4*>(orow_ptr[u] + g0 + c) = v;
             }
-            *reinterpret_cast<f32x4*>(orow_ptr[u] + g0 + c) = v;
           }
         }
       }
-    }
+    };
+    if (marks && (p.local_per_query || g0 < p.init_blocks ||
+                  (g0 + RG > max(0, w.sl + 1 - p.local_blocks) && g0 <= w.sl)))
+      write(std::true_type{});
+    else
+      write(std::false_type{});
   };
   if constexpr (Kd::is_fp4) {
     // Stages of two blocks, A = c0 + 2 sg and B = A + 1 (B may lie past the
