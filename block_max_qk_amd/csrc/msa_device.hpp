@@ -145,6 +145,17 @@ __device__ __forceinline__ float max_xor32(float x) {
   return __builtin_bit_cast(float, a);
 }
 
+// Lanes 0-31: max(a[l], a[l + 32]); lanes 32-63: max(b[l - 32], b[l]).  The
+// swap puts the upper half of a beside the lower half of b, so the lower
+// lanes hold both halves of a and the upper lanes both halves of b, and one
+// v_max_f32 finishes both (half the work of max_xor32 on each).
+__device__ __forceinline__ float max_pair32(float a, float b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a), y = __builtin_bit_cast(uint32_t, b);
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(x), "+v"(y));
+  return __builtin_bit_cast(float, x);
+}
+
 // max(x[l], x[l ^ 16]) in every lane l: v_permlane16_swap exchanges the odd
 // rows (16 lanes each) of its first register with the even rows of its
 // second, so two copies of x become each row pair's two rows side by side,

@@ -1258,12 +1258,12 @@ void prefill_kernel(Params p) {
     f32x4 run2[2];
     f32x16 acc2[2][NTW];
     auto finalize2 = [&](int bis, int bb) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) run2[bis][nt] = max_xor32(run2[bis][nt]);
       const int kk = (bb - w.c0) % RG;
+      // lanes of group G write N tile 2u + G: one swap and maximum per pair
 #pragma unroll
       for (int u = 0; u < NOUT; ++u)
-        resl[wave][u][kk][l] = (G && 2 * u + 1 < NTW) ? run2[bis][2 * u + 1] : run2[bis][2 * u];
+        resl[wave][u][kk][l] = max_pair32(run2[bis][2 * u],
+                                          run2[bis][2 * u + 1 < NTW ? 2 * u + 1 : 2 * u]);
       if (kk == RG - 1 || bb == vend - 1) pend = bb - kk;
     };
     for (int sg = 0; sg < nst2; ++sg) {
@@ -1513,13 +1513,12 @@ void prefill_kernel(Params p) {
       block(std::true_type{});
 
     if (off + ST == kP) {
-      // the two k groups hold the two halves of each 32-token M tile
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) run[nt] = max_xor32(run[nt]);
+      // the two k groups hold the two halves of each 32-token M tile; lanes
+      // of group G write N tile 2u + G: one swap and maximum per pair
       const int kk = (beta - w.c0) % RG;
 #pragma unroll
       for (int u = 0; u < NOUT; ++u) {
-        const float v = (G && 2 * u + 1 < NTW) ? run[2 * u + 1] : run[2 * u];
+        const float v = max_pair32(run[2 * u], run[2 * u + 1 < NTW ? 2 * u + 1 : 2 * u]);
 #pragma unroll
         for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
       }
