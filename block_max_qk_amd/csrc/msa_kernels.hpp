@@ -936,24 +936,24 @@ __global__ __launch_bounds__(256, (Kind<KK>::is_i8 || prefill_ntw(KK) >= 3) ? 2 
 void prefill_kernel(Params p) {
   using Kd = Kind<KK>;
   constexpr int NTW = prefill_ntw(KK);
-  // Key blocks pass through an LDS ring of stages.  16-bit keys: stages of 64
-  // tokens (16 KB), three deep, so a stage's copy has two compute periods to
-  // land; fp8: whole 128-token blocks (16 KB), two deep; MXFP4: two blocks
-  // (16 KB; their scales are staged for the whole work item up front), two
-  // deep; int8 (widened to fp16 through registers): whole blocks (32 KB), two
-  // deep.  All of it fits two workgroups per CU, three for fp8.
+  // Key blocks pass through a two-deep LDS ring of stages, one block per
+  // stage (MXFP4: two), so a stage's copy has the previous stage's compute
+  // to land: 16-bit keys 32 KB, fp8 16 KB, MXFP4 16 KB (their scales are
+  // staged for the whole work item up front), int8 widened to fp16 through
+  // registers, 32 KB.  All of it fits two workgroups per CU, three for fp8.
+  // (16-bit keys ran stages of 64 tokens in a three-deep ring before:
+  // whole-block stages halve the barriers and the per-stage work, and left
+  // the LDS room to bank a row's results eight blocks at a time; varlen
+  // bf16 prefill 3730 -> 3435 us in one A/B.)
   constexpr int RB = Kd::is_fp4 ? 64 : (Kd::is_f8 ? 128 : 256);   // LDS bytes per key token
   constexpr bool ASYNC = !Kd::is_i8;           // copy HBM/L2 -> LDS directly
   constexpr int BPS = Kd::is_fp4 ? 2 : 1;      // blocks per stage
-  constexpr int ST = Kd::is_fp4 ? BPS * kP : (ASYNC && RB == 256) ? 64 : kP;   // tokens per stage
-  constexpr int SPB = Kd::is_fp4 ? 1 : kP / ST;   // stages per block (MXFP4: see its loop)
-  constexpr int RING = SPB == 2 ? 3 : 2;
+  constexpr int ST = BPS * kP;                 // tokens per stage
+  constexpr int RING = 2;
   constexpr int SBYTES = ST * RB;
   constexpr int NI = SBYTES / 1024 / 4;        // copy instructions per wave per stage
-  static_assert(!ASYNC || RING == 2 || NI == 4,
-                "the three-deep ring's wait counts assume these copies per wave per stage");
   __shared__ __attribute__((aligned(16))) uint8_t kl[RING * SBYTES];
-  __shared__ float scl[2][kP];
+  __shared__ float scl[Kd::is_i8 ? 2 : 1][Kd::is_i8 ? kP : 1];
   // MXFP4: the scale words of every block of the work item, lane-major:
   // [block][n][mt] holds token 32 mt + n's word, so that lane (n, G) reads its
   // block's four M tiles with one 16-byte LDS read.  Copied once, before the
@@ -962,7 +962,8 @@ void prefill_kernel(Params p) {
   // every memory operation before using them.
   constexpr int CHUNK = prefill_chunk(KK);     // blocks per work item at most
   static_assert(CHUNK <= 64, "page indices are held one per lane");
-  __shared__ __attribute__((aligned(16))) uint32_t kmx[Kd::is_fp4 ? CHUNK : 1][32][4];
+  __shared__ __attribute__((aligned(16)))
+  uint32_t kmx[Kd::is_fp4 ? CHUNK : 1][Kd::is_fp4 ? 32 : 1][Kd::is_fp4 ? 4 : 1];
 
   const Work w = uniform_work(locate(p));
   if (!w.valid) return;
@@ -1051,7 +1052,7 @@ void prefill_kernel(Params p) {
 
   i32x4 st[4];
   float sv = 0.f;
-  // stage sg (block c0 + sg/SPB, tokens [off, off+ST)) into ring slot `slot`;
+  // stage sg (block c0 + sg; MXFP4 blocks c0 + 2 sg, + 1) into ring slot `slot`;
   // always exactly NI copy instructions per wave (the ring's waits count
   // them): token rows at or past kv_len copy row 0 of the block instead, which
   // the masked path discards
@@ -1060,9 +1061,10 @@ void prefill_kernel(Params p) {
   // This lane's byte offset within a stage for each of its wave's copy
   // instructions (token jl of the stage, swizzled 16-byte chunk c), computed
   // once per work item.
-  // (MXFP4: the copies of a wave are 16 rows apart and the swizzle does not
-  // see those row bits, so one offset serves all four)
-  constexpr int NCOF = Kd::is_fp4 ? 1 : ASYNC ? NI : 1;
+  // The swizzle repeats every 16 rows and a wave's copies are RPI rows apart,
+  // so copies 16 / RPI apart share a pattern: that many offsets (4 for
+  // 16-bit keys, 2 for fp8, 1 for MXFP4) and a row offset for the rest.
+  constexpr int NCOF = ASYNC ? (NI < 16 / RPI ? NI : 16 / RPI) : 1;
   uint32_t cof[NCOF];
 #pragma unroll
   for (int q = 0; q < NCOF; ++q) {
@@ -1082,8 +1084,7 @@ void prefill_kernel(Params p) {
   // the first, 2-3 the second, from the block base `kbytes` of their own
   // block, which may lie past the request's last block: then nothing is read)
   auto stage_copy = [&](int q, int sg, int slot, int64_t kbytes) {
-    const int beta = Kd::is_fp4 ? w.c0 + BPS * sg + (wave >> 1) : w.c0 + sg / SPB;
-    const int off = Kd::is_fp4 ? 0 : (sg % SPB) * ST;
+    const int beta = Kd::is_fp4 ? w.c0 + BPS * sg + (wave >> 1) : w.c0 + sg;
     // offsets within a block fit 32 bits (checked on the host)
     const uint8_t* kb = p.k + uniform64(kbytes + (int64_t)w.hk * p.k_head_stride);
     // (a scalar: computed in vector registers, the buffer descriptor made the
@@ -1092,8 +1093,8 @@ void prefill_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(kb), 0, nvalid * p.k_row_stride, kBufferWord3);
     const int X = wave * NI + q;
-    const uint32_t co = Kd::is_fp4 ? cof[0] + (uint32_t)(q * RPI * p.k_row_stride) : cof[q];
-    buffer_copy16_lds(rs, kl + slot * SBYTES + X * 1024, (uint32_t)(off * p.k_row_stride) + co);
+    const uint32_t co = cof[q % NCOF] + (uint32_t)((q / NCOF) * 16 * p.k_row_stride);
+    buffer_copy16_lds(rs, kl + slot * SBYTES + X * 1024, co);
   };
   // MXFP4: the scale words of the work item's nblk blocks, copied straight
   // into kmx: two copies per block, wave w taking blocks w, w + 4, ...; lane
@@ -1168,7 +1169,7 @@ void prefill_kernel(Params p) {
     oanc[u] = p.local_per_query ? query_anchor(w, i0 + oti) : w.sl;
   }
 
-  const int nst = busy ? (vend - w.c0) * SPB : 0;   // stages of this work item
+  const int nst = busy ? vend - w.c0 : 0;   // blocks of this work item (stages but MXFP4)
   if constexpr (ASYNC) {
     // the first block's page index is read before any copy is in flight
     // (MXFP4: the wave's own block of the first stage)
@@ -1176,9 +1177,7 @@ void prefill_kernel(Params p) {
     if constexpr (Kd::is_fp4) {
       if (nst > 0) stage_scales(vend - w.c0);
     }
-#pragma unroll
-    for (int sg = 0; sg < RING - 1; ++sg)
-      if (sg < nst) stage_async(sg, sg, sg < SPB ? kb0 : block_bytes(w.c0 + sg / SPB));
+    if (nst > 0) stage_async(0, 0, kb0);
     // (the loop's first barrier makes every wave's writes visible)
   } else {
     if (nst > 0) {
@@ -1194,18 +1193,17 @@ void prefill_kernel(Params p) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
   // Block results of this lane's row collect RG blocks at a time and are
-  // written as RG consecutive floats (16-byte stores).  16-bit keys run at
-  // the register limit and flush every 4 blocks; MXFP4 every 8, fp8 and int8
-  // every 16.
+  // written as RG consecutive floats (16-byte stores).  16-bit keys and
   // MXFP4: a block's result for each output row goes to a per-wave LDS area,
-  // one store per row, and the flush reads a row's RG values back; choosing
-  // the register of a block by its (uniform but not constant) position in the
-  // group takes a select per register and row, 32 VALU instructions per block
-  // against 32 MFMAs.  Groups of 8 blocks keep two workgroups within a CU's
-  // LDS.  (For fp8 the extra LDS array made the compiler wait for the next
-  // stage's copies before fragment reads in the block loop.)
-  constexpr bool LDS_RES = Kd::is_fp4;
-  constexpr int RG = (ASYNC && RB == 256) ? 4 : Kd::is_fp4 ? 8 : 16;
+  // one store per row, and the flush reads a row's RG values back (in
+  // registers, choosing the register of a block by its uniform but not
+  // constant position in the group takes a select per register and row, and
+  // the registers of 16-bit keys are full); groups of 8 blocks keep two
+  // workgroups within a CU's LDS.  fp8 and int8 hold 16 in registers (for fp8
+  // an LDS area made the compiler wait for the next stage's copies before
+  // fragment reads in the block loop).
+  constexpr bool LDS_RES = Kd::is_fp4 || (ASYNC && RB == 256);
+  constexpr int RG = LDS_RES ? 8 : 16;
   __shared__ float resl[LDS_RES ? kPrefillWaves : 1][LDS_RES ? NOUT : 1][LDS_RES ? RG : 1][64];
   float resv[NOUT][LDS_RES ? 1 : RG];
   int pend = -1;                 // first block of a group waiting to be written
@@ -1385,20 +1383,11 @@ void prefill_kernel(Params p) {
   } else {
   for (int sg = 0; sg < nst; ++sg) {
     const int slot = sg % RING;
-    const int beta = w.c0 + sg / SPB;
-    const int off = (sg % SPB) * ST;
-    // Stage sg has landed (the one copy still allowed in flight is the next
-    // stage's) and every wave is done with the slot the copy below reuses.
-    // Written out because a plain __syncthreads() would wait for all copies.
-    // (the next stage's NI copies may stay in flight)
-    if (RING == 3 && sg + 1 < nst) {
-      if constexpr (NI == 4)
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+    const int beta = w.c0 + sg;
+    // Stage sg has landed (every wave's copies) and every wave is done with
+    // the slot the copy below reuses.  Written out because __syncthreads()
+    // leaves the wait to the compiler.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // a finished group of results is written here, ahead of the next
     // copies, so that the copies stay the newest memory operations the
     // waits count
@@ -1406,22 +1395,20 @@ void prefill_kernel(Params p) {
       flush(pend);
       pend = -1;
     }
-    // The copy of stage sg + RING - 1 (into the slot every wave has just
-    // left) is issued from inside this stage's compute, spread over it where
+    // The copy of stage sg + 1 (into the slot every wave has just left) is
+    // issued from inside this stage's compute, spread over it where
     // registers allow: issued all at once after the barrier, the copies of a
     // workgroup's four waves stalled instruction issue for hundreds of
     // cycles.
-    const int csg = sg + RING - 1;
+    const int csg = sg + 1;
     const bool copy_next = csg < nst;
-    const int64_t ckb = (ASYNC && copy_next) ? block_bytes(w.c0 + csg / SPB) : 0;
+    const int64_t ckb = (ASYNC && copy_next) ? block_bytes(w.c0 + csg) : 0;
     if constexpr (!ASYNC) {
       if (copy_next) gload_i8(beta + 1);
     }
     const uint8_t* kc = kl + slot * SBYTES;
-    if (off == 0) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
-    }
+    for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
     // One pass over the block's four 32-token M tiles; MASKED selects -inf for
     // key tokens past each row's last visible one (only blocks cut by the
     // window or by kv_len need it).  The branch below is uniform per block.
@@ -1487,7 +1474,7 @@ void prefill_kernel(Params p) {
           // acc[nt][r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int jr = off + mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+            const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
             float sc = 1.f;
             if constexpr (Kd::is_i8) sc = scl[slot][jr];
 #pragma unroll
@@ -1512,15 +1499,19 @@ void prefill_kernel(Params p) {
     else
       block(std::true_type{});
 
-    if (off + ST == kP) {
+    {
       // the two k groups hold the two halves of each 32-token M tile; lanes
       // of group G write N tile 2u + G: one swap and maximum per pair
       const int kk = (beta - w.c0) % RG;
 #pragma unroll
       for (int u = 0; u < NOUT; ++u) {
         const float v = max_pair32(run[2 * u], run[2 * u + 1 < NTW ? 2 * u + 1 : 2 * u]);
+        if constexpr (LDS_RES) {
+          resl[wave][u][kk][l] = v;
+        } else {
 #pragma unroll
-        for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+          for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+        }
       }
       if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
     }
