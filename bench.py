@@ -10,7 +10,12 @@ head, kv_len ~ U[1, 32768], bf16 keys in 16384 paged 128-token blocks
 Timed region: W untimed warmup steps, then exactly K steps bracketed by
 torch.cuda.synchronize(); one pair of HIP events on the launch stream around
 the K launches (nothing recorded between them) gives the kernel's average
-duration for the roofline.
+duration for the roofline.  The launches are a loop of C-ABI calls from
+Python; each line also reports, under 'graph', the same K calls captured
+into a HIP graph and replayed once (the GPU-side figure where the host's
+call rate, ~8-18 us a call depending on the box, is slower than a short
+kernel; where the host keeps up, replays measured no faster, so the loop is
+the primary figure; ``--graph`` swaps them).
 To keep the 256 MB Infinity Cache from serving repeated reads, the key cache
 is replicated into several HBM copies and the steps rotate over them.
 
@@ -105,6 +110,42 @@ def workload_stats(case) -> dict:
             "k_bytes": k_bytes, "q_bytes": q_bytes, "out_bytes": out_bytes}
 
 
+def time_launches(launch, steps: int, stream, graph: bool):
+    """Time `steps` launches, launch(i, stream_handle) issuing launch i on the
+    given stream.  graph: the launches are captured once into a HIP graph and
+    the timed region is one replay of it (the K kernel launches with no host
+    work between them); otherwise a plain loop of C-ABI calls from Python.
+    Returns the average launch duration from one HIP event pair around the K
+    launches on `stream` (nothing recorded between them: events between
+    launches add their own processing time to each) and the wall time per
+    step; both bracketed by torch.cuda.synchronize()."""
+    import torch
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(steps):
+                launch(i, cap.cuda_stream)
+        stream.wait_stream(cap)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph:
+        with torch.cuda.stream(stream):
+            g.replay()
+    else:
+        for i in range(steps):
+            launch(i, stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return e0.elapsed_time(e1) / steps, (t1 - t0) * 1e3 / steps
+
+
 def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                  cpu_baseline: bool, args, local_mode: int = 0, topk: bool = False,
                  host: dict = None) -> dict:
@@ -161,8 +202,7 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
                           ctypes.c_void_p(kv.data_ptr()), case.batch, case.block_size,
                           m._binding.LAYOUT_CODE[case.layout], case.sparse_mode,
                           case.init_blocks, case.local_blocks, case.local_mode,
-                          ctypes.c_void_p(out.data_ptr()), W,
-                          ctypes.c_void_p(stream.cuda_stream)))
+                          ctypes.c_void_p(out.data_ptr()), W, None))
             continue
         a = (ctypes.byref(qd), ctypes.byref(kd), ctypes.c_void_p(sl.data_ptr()),
              None if bt is None else ctypes.c_void_p(bt.data_ptr()), case.max_blocks,
@@ -171,33 +211,23 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
              case.block_size, m._binding.LAYOUT_CODE[case.layout], case.sparse_mode,
              case.init_blocks,
              case.local_blocks, case.local_mode, ctypes.c_void_p(out.data_ptr()), W,
-             ctypes.c_void_p(stream.cuda_stream), family)
+             None, family)
         calls.append(a)
     fn = lib.msa_index_score_mxfp4 if mx else lib.msa_index_score_ex
+    si = 18 if mx else 17          # position of the stream argument
 
-    def step(i):
-        st = fn(*calls[i % copies])
+    def launch(i, h):
+        a = calls[i % copies]
+        st = fn(*a[:si], ctypes.c_void_p(h), *a[si + 1:])
         if st != 0:
             raise RuntimeError(m.msa_status_str(st))
 
     for i in range(warmup):
-        step(i)
+        launch(i, stream.cuda_stream)
     torch.cuda.synchronize()
-    # one HIP event pair around the K launches on the launch stream, nothing
-    # between them: the average launch duration (events between launches add
-    # their own processing time to each)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernel_ms = e0.elapsed_time(e1) / steps
-    ms_per_step = (t1 - t0) * 1e3 / steps
+    graph = bool(getattr(args, "graph", False))
+    kernel_ms, ms_per_step = time_launches(launch, steps, stream, graph)
+    alt_ms, alt_step = time_launches(launch, steps, stream, not graph)
 
     gbs = stats["bytes"] / (kernel_ms * 1e-3) / 1e9
     tflops = stats["flops"] / (kernel_ms * 1e-3) / 1e12
@@ -233,22 +263,26 @@ def bench_config(c_idx: int, steps: int, warmup: int, copies: int, family: int,
         "block_scores_per_step": stats["scores"], "out_entries_per_step": stats["out_entries"],
         "roofline": roof,
         "cpu_baseline": None,
+        "launch": "hip_graph" if graph else "eager",
+        ("eager" if graph else "graph"): {"kernel_ms_avg": round(alt_ms, 5),
+                                          "ms_per_step": round(alt_step, 5)},
         "input_generation_s": round(t_gen, 2),
     }
     if topk:
         # the selection that follows the operator, timed on the scores the
         # last step wrote (resident in HBM)
-        res["topk"] = time_topk(out, case.max_blocks, steps, warmup, stream)
+        res["topk"] = time_topk(out, case.max_blocks, steps, warmup, stream, graph=graph)
     del calls, keep, out
     if cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_leg(case, stats, args, host or host_cpu())
     return res
 
 
-def time_topk(scores, num_valid: int, steps: int, warmup: int, stream, k: int = 16) -> dict:
+def time_topk(scores, num_valid: int, steps: int, warmup: int, stream, k: int = 16,
+              graph: bool = True) -> dict:
     """msa_block_topk (k = 16) over every row of a score tensor already in
-    HBM: average launch duration from one event pair around the launches, and
-    its HBM roofline (each row's num_valid scores read, k indices written)."""
+    HBM: average launch duration (time_launches), and its HBM roofline (each
+    row's num_valid scores read, k indices written)."""
     import torch
     import block_max_qk_amd as m
     Hq, T, W = scores.shape
@@ -256,14 +290,8 @@ def time_topk(scores, num_valid: int, steps: int, warmup: int, stream, k: int = 
     for _ in range(warmup):
         m.msa_block_topk(scores, num_valid, k, out, stream=stream)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        m.msa_block_topk(scores, num_valid, k, out, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, _ = time_launches(lambda i, h: m.msa_block_topk(scores, num_valid, k, out, stream=h),
+                          steps, stream, graph)
     alg = Hq * T * (num_valid + k) * 4
     gbs = alg / (ms * 1e-3) / 1e9
     return {"kernel": "topk_kernel", "k": k, "rows": Hq * T, "num_valid": num_valid,
@@ -432,17 +460,9 @@ def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) ->
     for _ in range(warmup):
         m.msa_block_topk(scores, nv, k, out, stream=stream)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        m.msa_block_topk(scores, nv, k, out, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernel_ms = e0.elapsed_time(e1) / steps
-    ms_per_step = (t1 - t0) * 1e3 / steps
+    graph = bool(getattr(args, "graph", False))
+    kernel_ms, ms_per_step = time_launches(
+        lambda i, h: m.msa_block_topk(scores, nv, k, out, stream=h), steps, stream, graph)
     alg = rows * (nv + k) * 4      # each row's num_valid scores read, k indices written
     gbs = alg / (kernel_ms * 1e-3) / 1e9
     res = {
@@ -452,6 +472,7 @@ def bench_topk(c_idx: int, steps: int, warmup: int, cpu_baseline: bool, args) ->
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": case.name, "stage": "top-k", "k": k, "rows": rows,
                    "width": W, "num_valid": nv},
+        "launch": "hip_graph" if graph else "eager",
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("topk:" + case.name),
@@ -569,7 +590,8 @@ def bench_decode_batch(B: int, steps: int, warmup: int, seed: int = 20261299) ->
 def workload_summary(r: dict) -> dict:
     """One workload's figures for the headline line's 'workloads' list."""
     keys = ("value", "unit", "ms_per_step", "dtype", "hbm_gbs", "mfma_tflops",
-            "block_scores_per_step", "out_entries_per_step", "roofline", "cpu_baseline", "topk")
+            "block_scores_per_step", "out_entries_per_step", "roofline", "cpu_baseline", "topk",
+            "launch", "eager", "graph")
     out = {"workload": r["config"]["workload"], "config": r["config"]}
     out.update({k: r[k] for k in keys if k in r})
     out["kernel_ms_avg"] = r["roofline"]["kernel_ms_avg"]
@@ -592,6 +614,10 @@ def main():
                          "so that the 256 MB Infinity Cache cannot serve a step from the "
                          "one before; 1 otherwise)")
     ap.add_argument("--family", type=int, default=-1, help="-1 auto, 0 decode, 1 prefill tiles")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K launches as one replay of a HIP graph that holds them "
+                         "instead of a loop of C-ABI calls from Python (each line reports "
+                         "the other way's figures too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="whole output rows of a prefill workload the oracle computes for "
