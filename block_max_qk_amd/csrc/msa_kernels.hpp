@@ -1346,8 +1346,9 @@ void prefill_kernel(Params p) {
           }
 #pragma unroll
           for (int nt = 0; nt < NTW; ++nt)
-            ac[nt] = q == 0 ? mfma32x32x64_fp4_sel<0, 0>(f[i], qv[nt][0], ac[nt], ksw[bis][mt], qsw[nt])
-                            : mfma32x32x64_fp4_sel<2, 1>(f[i], qv[nt][1], ac[nt], ksw[bis][mt], qsw[nt]);
+            ac[nt] = q == 0
+                ? mfma32x32x64_fp4_sel<0, 0>(f[i], qv[nt][0], ac[nt], ksw[bis][mt], qsw[nt])
+                : mfma32x32x64_fp4_sel<2, 1>(f[i], qv[nt][1], ac[nt], ksw[bis][mt], qsw[nt]);
           if (k > 0) {
             // tile k - 1 (the other block's), half of its N tiles per fragment
             const int pb = (k - 1) & 1, pm = (k - 1) >> 1;
@@ -1381,146 +1382,146 @@ void prefill_kernel(Params p) {
     }
     if (pend >= 0) flush(pend);
   } else {
-  for (int sg = 0; sg < nst; ++sg) {
-    const int slot = sg % RING;
-    const int beta = w.c0 + sg;
-    // Stage sg has landed (every wave's copies) and every wave is done with
-    // the slot the copy below reuses.  Written out because __syncthreads()
-    // leaves the wait to the compiler.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // a finished group of results is written here, ahead of the next
-    // copies, so that the copies stay the newest memory operations the
-    // waits count
-    if (pend >= 0) {
-      flush(pend);
-      pend = -1;
-    }
-    // The copy of stage sg + 1 (into the slot every wave has just left) is
-    // issued from inside this stage's compute, spread over it where
-    // registers allow: issued all at once after the barrier, the copies of a
-    // workgroup's four waves stalled instruction issue for hundreds of
-    // cycles.
-    const int csg = sg + 1;
-    const bool copy_next = csg < nst;
-    const int64_t ckb = (ASYNC && copy_next) ? block_bytes(w.c0 + csg) : 0;
-    if constexpr (!ASYNC) {
-      if (copy_next) gload_i8(beta + 1);
-    }
-    const uint8_t* kc = kl + slot * SBYTES;
+    for (int sg = 0; sg < nst; ++sg) {
+      const int slot = sg % RING;
+      const int beta = w.c0 + sg;
+      // Stage sg has landed (every wave's copies) and every wave is done with
+      // the slot the copy below reuses.  Written out because __syncthreads()
+      // leaves the wait to the compiler.
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // a finished group of results is written here, ahead of the next
+      // copies, so that the copies stay the newest memory operations the
+      // waits count
+      if (pend >= 0) {
+        flush(pend);
+        pend = -1;
+      }
+      // The copy of stage sg + 1 (into the slot every wave has just left) is
+      // issued from inside this stage's compute, spread over it where
+      // registers allow: issued all at once after the barrier, the copies of a
+      // workgroup's four waves stalled instruction issue for hundreds of
+      // cycles.
+      const int csg = sg + 1;
+      const bool copy_next = csg < nst;
+      const int64_t ckb = (ASYNC && copy_next) ? block_bytes(w.c0 + csg) : 0;
+      if constexpr (!ASYNC) {
+        if (copy_next) gload_i8(beta + 1);
+      }
+      const uint8_t* kc = kl + slot * SBYTES;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
-    // One pass over the block's four 32-token M tiles; MASKED selects -inf for
-    // key tokens past each row's last visible one (only blocks cut by the
-    // window or by kv_len need it).  The branch below is uniform per block.
-    auto block = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
-      // Key fragments (MFMA A operand), 16 bytes each, in the order they are
-      // consumed: M tile mt (32 tokens), k step s, and for fp8 the two halves
-      // of a 32-byte operand.  Fragment i + LEAD is read from LDS while
-      // fragment i feeds the MFMAs, which hides the LDS latency with only
-      // LEAD + 1 fragments live.
-      constexpr int PER_MT = Kd::is_f8 ? 4 : 8;   // fragments per M tile
-      constexpr int NFR = (ST / 32) * PER_MT;
-      constexpr int LEAD = Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
-      auto frag = [&](int i) -> i32x4 {
-        const int mt = i / PER_MT, q = i % PER_MT;
-        const int jj = mt * 32 + n;
-        if constexpr (Kd::is_f8) {
-          // q = 2*s + half: bytes [64s + 32G + 16*half, +16) of the token
-          const int c = 4 * (q >> 1) + 2 * G + (q & 1);
-          return *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ ((jj >> 1) & 7)) << 4));
-        } else {
-          const int c = 2 * q + G;
-          return *reinterpret_cast<const i32x4*>(kc + jj * 256 + ((c ^ (jj & 15)) << 4));
-        }
-      };
-      i32x4 f[NFR];
-#pragma unroll
-      for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
-      f32x16 acc[NTW];
-#pragma unroll
-      for (int i = 0; i < NFR; ++i) {
-        if constexpr (ASYNC) {
-          // copy points per stage: two for 16-bit keys; one for fp8, whose
-          // three waves per SIMD leave no registers for more
-          constexpr int CPTS = RB == 256 ? 2 : 1;
-          static_assert(NFR % CPTS == 0 && NI % CPTS == 0, "copies spread evenly");
-          if (copy_next && i % (NFR / CPTS) == 0) {
-#pragma unroll
-            for (int q = 0; q < NI / CPTS; ++q)
-              stage_copy((i / (NFR / CPTS)) * (NI / CPTS) + q, csg, csg % RING, ckb);
+      for (int nt = 0; nt < 4; ++nt) run[nt] = -__builtin_inff();
+      // One pass over the block's four 32-token M tiles; MASKED selects -inf for
+      // key tokens past each row's last visible one (only blocks cut by the
+      // window or by kv_len need it).  The branch below is uniform per block.
+      auto block = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        // Key fragments (MFMA A operand), 16 bytes each, in the order they are
+        // consumed: M tile mt (32 tokens), k step s, and for fp8 the two halves
+        // of a 32-byte operand.  Fragment i + LEAD is read from LDS while
+        // fragment i feeds the MFMAs, which hides the LDS latency with only
+        // LEAD + 1 fragments live.
+        constexpr int PER_MT = Kd::is_f8 ? 4 : 8;   // fragments per M tile
+        constexpr int NFR = (ST / 32) * PER_MT;
+        constexpr int LEAD = Kd::is_f8 ? 4 : (NTW >= 3 ? 1 : 2);
+        auto frag = [&](int i) -> i32x4 {
+          const int mt = i / PER_MT, q = i % PER_MT;
+          const int jj = mt * 32 + n;
+          if constexpr (Kd::is_f8) {
+            // q = 2*s + half: bytes [64s + 32G + 16*half, +16) of the token
+            const int c = 4 * (q >> 1) + 2 * G + (q & 1);
+            return *reinterpret_cast<const i32x4*>(kc + jj * 128 + ((c ^ ((jj >> 1) & 7)) << 4));
+          } else {
+            const int c = 2 * q + G;
+            return *reinterpret_cast<const i32x4*>(kc + jj * 256 + ((c ^ (jj & 15)) << 4));
           }
-        }
-        if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
-        const int mt = i / PER_MT, q = i % PER_MT;
-        if (q == 0) {
+        };
+        i32x4 f[NFR];
 #pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x16{};
-        }
-        if constexpr (Kd::is_f8) {
-          if (q & 1) {
-            const int s = q >> 1;
-            const i32x8 a = cat(f[i - 1], f[i]);
+        for (int i = 0; i < LEAD; ++i) f[i] = frag(i);
+        f32x16 acc[NTW];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-              acc[nt] = mfma32x32x64_f8<KK>(a, cat(qv[nt][2 * s], qv[nt][2 * s + 1]), acc[nt]);
-          }
-        } else {
+        for (int i = 0; i < NFR; ++i) {
+          if constexpr (ASYNC) {
+            // copy points per stage: two for 16-bit keys; one for fp8, whose
+            // three waves per SIMD leave no registers for more
+            constexpr int CPTS = RB == 256 ? 2 : 1;
+            static_assert(NFR % CPTS == 0 && NI % CPTS == 0, "copies spread evenly");
+            if (copy_next && i % (NFR / CPTS) == 0) {
 #pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-            acc[nt] = mfma32x32x16<Kd::mfma_kind>(f[i], qv[nt][q], acc[nt]);
-        }
-        if (q == PER_MT - 1) {
-          // acc[nt][r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
-            float sc = 1.f;
-            if constexpr (Kd::is_i8) sc = scl[slot][jr];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-              float v = acc[nt][r];
-              if constexpr (Kd::is_i8) v *= sc;
-              if constexpr (MASKED) {
-                const int j = beta * kP + jr;
-                v = (j <= lim[nt]) ? v : -__builtin_inff();
-              }
-              run[nt] = fmaxf(run[nt], v);
+              for (int q = 0; q < NI / CPTS; ++q)
+                stage_copy((i / (NFR / CPTS)) * (NI / CPTS) + q, csg, csg % RING, ckb);
             }
           }
-        }
-        // keep this shape: one fragment read, its MFMAs, (an epilogue); the
-        // compiler would otherwise hoist every read and run out of registers
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    if (beta * kP + kP - 1 <= lim_lo)
-      block(std::false_type{});
-    else
-      block(std::true_type{});
-
-    {
-      // the two k groups hold the two halves of each 32-token M tile; lanes
-      // of group G write N tile 2u + G: one swap and maximum per pair
-      const int kk = (beta - w.c0) % RG;
+          if (i + LEAD < NFR) f[i + LEAD] = frag(i + LEAD);
+          const int mt = i / PER_MT, q = i % PER_MT;
+          if (q == 0) {
 #pragma unroll
-      for (int u = 0; u < NOUT; ++u) {
-        const float v = max_pair32(run[2 * u], run[2 * u + 1 < NTW ? 2 * u + 1 : 2 * u]);
-        if constexpr (LDS_RES) {
-          resl[wave][u][kk][l] = v;
-        } else {
+            for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x16{};
+          }
+          if constexpr (Kd::is_f8) {
+            if (q & 1) {
+              const int s = q >> 1;
+              const i32x8 a = cat(f[i - 1], f[i]);
 #pragma unroll
-          for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+              for (int nt = 0; nt < NTW; ++nt)
+                acc[nt] = mfma32x32x64_f8<KK>(a, cat(qv[nt][2 * s], qv[nt][2 * s + 1]), acc[nt]);
+            }
+          } else {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+              acc[nt] = mfma32x32x16<Kd::mfma_kind>(f[i], qv[nt][q], acc[nt]);
+          }
+          if (q == PER_MT - 1) {
+            // acc[nt][r] holds key token mt*32 + 8*(r/4) + 4*G + r%4 of row n
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int jr = mt * 32 + 8 * (r >> 2) + 4 * G + (r & 3);
+              float sc = 1.f;
+              if constexpr (Kd::is_i8) sc = scl[slot][jr];
+#pragma unroll
+              for (int nt = 0; nt < NTW; ++nt) {
+                float v = acc[nt][r];
+                if constexpr (Kd::is_i8) v *= sc;
+                if constexpr (MASKED) {
+                  const int j = beta * kP + jr;
+                  v = (j <= lim[nt]) ? v : -__builtin_inff();
+                }
+                run[nt] = fmaxf(run[nt], v);
+              }
+            }
+          }
+          // keep this shape: one fragment read, its MFMAs, (an epilogue); the
+          // compiler would otherwise hoist every read and run out of registers
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
-    }
-    if constexpr (!ASYNC) {
-      if (sg + 1 < nst) lstore_i8(slot ^ 1);
-    }
-  }
+      };
+      if (beta * kP + kP - 1 <= lim_lo)
+        block(std::false_type{});
+      else
+        block(std::true_type{});
 
-  if (pend >= 0) flush(pend);
+      {
+        // the two k groups hold the two halves of each 32-token M tile; lanes
+        // of group G write N tile 2u + G: one swap and maximum per pair
+        const int kk = (beta - w.c0) % RG;
+#pragma unroll
+        for (int u = 0; u < NOUT; ++u) {
+          const float v = max_pair32(run[2 * u], run[2 * u + 1 < NTW ? 2 * u + 1 : 2 * u]);
+          if constexpr (LDS_RES) {
+            resl[wave][u][kk][l] = v;
+          } else {
+#pragma unroll
+            for (int k = 0; k < RG; ++k) resv[u][k] = (k == kk) ? v : resv[u][k];
+          }
+        }
+        if (kk == RG - 1 || beta == vend - 1) pend = beta - kk;
+      }
+      if constexpr (!ASYNC) {
+        if (sg + 1 < nst) lstore_i8(slot ^ 1);
+      }
+    }
+
+    if (pend >= 0) flush(pend);
   }
   // columns of the work item past the last group: -inf and local_mask
   fill_tile_columns(p, w, i0, w.c0 + ((vend - w.c0 + RG - 1) / RG) * RG, w.c1);
