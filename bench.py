@@ -22,12 +22,13 @@ is replicated into several HBM copies and the steps rotate over them.
 Output: one JSON line (rank 0 of 1).  By default its top level is the
 headline decode batch, and its ``workloads`` list holds all five base
 workloads measured in the same process (the tiny example, the decode batch,
-the varlen prefill, the int8 decode batch and the chunked fp8 prefill), each
-with its average launch duration, roofline (with HBM traffic from the
+the varlen prefill, the int8 decode batch and the chunked fp8 prefill) and
+the MXFP4 variants of three of them (the decode batch and both prefills),
+each with its average launch duration, roofline (with HBM traffic from the
 committed counter runs when they match the current kernel sources), the
 oracle's CPU baseline on this host's available cores (one core too, for the
-decode-sized ones) and, for the prefill workloads, the top-k selection on
-their scores.  ``--config all`` prints one full line per workload instead.
+decode-sized ones) and, for the base prefill workloads, the top-k selection
+on their scores.  ``--config all`` prints one full line per workload instead.
 ``--topk`` times the top-k block selection (msa_block_topk, k = 16) over the
 chosen workload's score rows instead, with its own roofline (HBM bytes: every
 row's num_valid scores read, its k indices written).  ``--local-mode query``
@@ -605,8 +606,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="default",
-                    help="'default': the headline decode line with every base workload "
-                         "measured in the same process under 'workloads'; or a workload "
+                    help="'default': the headline decode line with every workload (the "
+                         "five base ones and three MXFP4 variants) measured in the same "
+                         "process under 'workloads'; or a workload "
                          "name or index, 'all' (one line per base workload) or 'mx' (their "
                          "MXFP4 variants)")
     ap.add_argument("--copies", type=int, default=0,
@@ -671,12 +673,13 @@ def main():
     if args.config == "default":
         host = host_cpu() if not args.no_cpu_baseline else None
         recs = []
-        for c, name in enumerate(synth.CONFIG_NAMES):
+        for c, name in enumerate(names):
             copies = args.copies if args.copies > 0 else (4 if name.startswith("decode") else 1)
             print(f"[bench] {name}", file=sys.stderr, flush=True)
+            base = c < len(synth.CONFIG_NAMES)
             recs.append(bench_config(c, args.steps, args.warmup, copies, args.family,
                                      not args.no_cpu_baseline, args, local_mode=local_mode,
-                                     topk=name.startswith("prefill"), host=host))
+                                     topk=base and name.startswith("prefill"), host=host))
         head = dict(next(r for r in recs if r["config"]["workload"] == HEADLINE))
         head["workloads"] = [workload_summary(r) for r in recs]
         print(json.dumps(head), flush=True)
