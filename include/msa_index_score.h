@@ -139,7 +139,9 @@ typedef struct {
  * memory.  The only state it keeps between calls is one figure per device,
  * key type and batch kind (at most 64 requests, or more): the decode
  * kernel's workgroup slot count (CU count times occupancy), asked of the HIP
- * runtime on the first such decode launch on that device.  Returns MSA_OK
+ * runtime on the first such decode launch on that device (read and written
+ * atomically).  Calls may overlap, from several host threads and on the same
+ * or different streams: they share no device memory.  Returns MSA_OK
  * or an error status; T = 0 returns MSA_OK without launching anything.
  * MSA_ERR_HIP reports a failure of this call's own runtime queries or
  * launch, never an error pending from earlier HIP work.  query, key and out
