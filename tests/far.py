@@ -152,3 +152,15 @@ def far_output_case():
                            kv_lens=[700, 5000, 130], Hq=8, Hkv=2, qdtype="bf16", layout="TND",
                            MB=FAR_OUT_MB, init_blocks=1, local_blocks=3,
                            start_loc=[W - 6, 2, W - 1])
+
+
+def long_context_case():
+    """Two requests past a million keys (8193 and 11719 blocks): a one-token
+    decode and a three-token speculative step, 8 heads over one KV head, bf16
+    keys in 19912 pages (1.2 GB) behind a random table.  Each request's work
+    list and output row run to ~12k blocks, and the top-k selection on its
+    rows takes the search over rows longer than 2048 blocks."""
+    import synth
+    return synth.make_case("long_ctx_bbnd_bf16", 8400, q_lens=[1, 3],
+                           kv_lens=[(1 << 20) + 77, 1_500_000], Hq=8, Hkv=1, qdtype="bf16",
+                           layout="BBND", init_blocks=1, local_blocks=2)

@@ -11,7 +11,9 @@ kernel families:
 * packed keys (bf16, int8, MXFP4) whose requests follow a 4 GiB key segment;
 * an output of 8 x 20 x 2^24 float32 (10.7 GB, the largest output width), the
   local_mask windows of two requests at its last columns, and the top-k
-  selection over its full rows.
+  selection over its full rows;
+* two requests past a million keys (a decode token and a speculative step),
+  compared whole, with the top-k selection on their ~12k-block rows.
 
 The far inputs are the small cases of tests/far.py placed so that the result
 is unchanged (checked with the oracle on the CPU in test_far_cpu.py), so the
@@ -145,4 +147,36 @@ def test_far_output_and_topk(family, dev, far_out):
     tau = tol * float(ref[:, :, :64][fin].abs().max())
     differ, bad = _sets_differ_beyond_near_ties(g, w, rows_ref, tau)
     log(f"[gpu] far output top-k: {Hq * T} rows, {differ} near-tie rows, {bad} beyond")
+    assert bad == 0 and differ <= 2
+
+
+@pytest.fixture(scope="module")
+def long_ctx():
+    case = far.long_context_case()
+    return case, oracle.index_score_case(case)
+
+
+@pytest.mark.parametrize("family", [0, 1])
+def test_long_context_and_topk(family, dev, long_ctx):
+    import block_max_qk_amd as m
+    from test_parity_gpu import run_gpu, to_device
+    from test_topk_gpu import _sets_differ_beyond_near_ties
+    case, ref = long_ctx
+    Hq, T, W = ref.shape
+    log(f"[gpu] long context family={family}: kv_len {case.kv_len.tolist()}, [{Hq}, {T}, {W}]")
+    got = run_gpu(case, dev, family)
+    r = check(ref, got, tol_of(case))
+    assert r["ok"], r
+    # top-k on the GPU scores against the oracle's selection on its own
+    k = 16
+    sel = torch.full((T, Hq, k), -7, dtype=torch.int32, device=dev)
+    m.msa_block_topk(got.to(dev), case.max_blocks, k, sel)
+    torch.cuda.synchronize()
+    want = oracle.block_topk(ref, case.max_blocks, k)
+    g = sel.cpu().permute(1, 0, 2).reshape(Hq * T, k)
+    w = want.permute(1, 0, 2).reshape(Hq * T, k)
+    fin = torch.isfinite(ref) & (ref.abs() < 1e28)
+    tau = tol_of(case) * float(ref[fin].abs().max())
+    differ, bad = _sets_differ_beyond_near_ties(g, w, ref.reshape(Hq * T, W), tau)
+    log(f"[gpu] long context top-k: {Hq * T} rows, {differ} near-tie rows, {bad} beyond")
     assert bad == 0 and differ <= 2
