@@ -12,6 +12,7 @@ from .inputs import (  # noqa: F401
     MX_CONFIG_NAMES,
     config_case,
     mx_config_case,
+    e5m2_config_case,
     make_case,
     edge_cases,
     random_cases,

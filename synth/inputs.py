@@ -342,6 +342,15 @@ def config_case(c: int) -> MsaCase:
     raise IndexError(c)
 
 
+def e5m2_config_case() -> MsaCase:
+    """The chunked fp8 prefill workload with e5m2 query and key instead of
+    e4m3: 4096 tokens after a 126976-token prefix, Hq = 64 over Hkv = 8,
+    1024 paged blocks (drawn from its own seed)."""
+    return make_case("prefill_bbnd_f8e5m2", 20261206, q_lens=[4096], kv_lens=[131072], Hq=64,
+                     Hkv=8, qdtype="f8e5m2", layout="BBND", MB=1024, NP=1024, table="perm",
+                     sparse_mode=3, init_blocks=1, local_blocks=4)
+
+
 # The MXFP4 variants of three workloads: the same shapes, lengths and tables,
 # with MXFP4 query and key (N(0,1) encoded per 32-element group).
 MX_CONFIG_NAMES = ("decode_bbnd_mxfp4", "prefill_tnd_mxfp4", "prefill_bbnd_mxfp4")

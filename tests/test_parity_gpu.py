@@ -328,6 +328,24 @@ def test_full_size_per_query_local_window(c_idx, dev):
         assert bool((own[:, pos >= 0] == 1e29).all()), c.name
 
 
+def test_full_size_e5m2(dev):
+    # The chunked fp8 prefill with e5m2 operands (the other OCP fp8 format,
+    # same kernels): stratified full rows and random entries.
+    c = synth.e5m2_config_case()
+    log(f"[gpu] config {c.name}")
+    got = run_gpu(c, dev)
+    pts, nrows = _sample_points(c, got.shape, 256, 10000, 555)
+    ref = oracle.index_score_case_points(c, pts)
+    gv = got[pts[:, 0], pts[:, 1], pts[:, 2]]
+    W = got.shape[2]
+    nfull = nrows * W
+    assert len({(h // (c.Hq // c.Hkv)) for h, _ in stratified_rows(c, 256, 555)}) == c.Hkv
+    assert_rows_match(ref[:nfull].reshape(nrows, W), gv[:nfull].reshape(nrows, W), tol_of(c),
+                      f"{c.name} {nrows} full rows")
+    r2 = compare_values(ref[nfull:], gv[nfull:], tol_of(c))
+    assert r2["ok"], r2
+
+
 @pytest.mark.parametrize("name", ["decode_bbnd_mxfp4", "prefill_tnd_mxfp4",
                                   "prefill_bbnd_mxfp4"])
 def test_full_size_mxfp4(name, dev):
