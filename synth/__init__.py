@@ -13,6 +13,7 @@ from .inputs import (  # noqa: F401
     config_case,
     mx_config_case,
     e5m2_config_case,
+    i8_prefill_config_case,
     make_case,
     edge_cases,
     random_cases,

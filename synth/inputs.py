@@ -351,6 +351,18 @@ def e5m2_config_case() -> MsaCase:
                      sparse_mode=3, init_blocks=1, local_blocks=4)
 
 
+def i8_prefill_config_case() -> MsaCase:
+    """The varlen prefill workload with an fp16 query and int8 packed keys
+    with their per-token scales: requests of 1K, 2K, 4K and 8K tokens after
+    prefixes of 0, 4K, 16K and 56K keys, Hq = 32 over Hkv = 4."""
+    q_lens = [1024, 2048, 4096, 8192]
+    prefix = [0, 4096, 16384, 57344]
+    kv = [p + q for p, q in zip(prefix, q_lens)]
+    return make_case("prefill_tnd_i8", 20261207, q_lens=q_lens, kv_lens=kv, Hq=32, Hkv=4,
+                     qdtype="f16", kdtype="i8", layout="TND", sparse_mode=3, init_blocks=1,
+                     local_blocks=2)
+
+
 # The MXFP4 variants of three workloads: the same shapes, lengths and tables,
 # with MXFP4 query and key (N(0,1) encoded per 32-element group).
 MX_CONFIG_NAMES = ("decode_bbnd_mxfp4", "prefill_tnd_mxfp4", "prefill_bbnd_mxfp4")

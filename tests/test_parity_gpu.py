@@ -328,10 +328,12 @@ def test_full_size_per_query_local_window(c_idx, dev):
         assert bool((own[:, pos >= 0] == 1e29).all()), c.name
 
 
-def test_full_size_e5m2(dev):
+@pytest.mark.parametrize("which", ["e5m2", "i8"])
+def test_full_size_variant(which, dev):
     # The chunked fp8 prefill with e5m2 operands (the other OCP fp8 format,
-    # same kernels): stratified full rows and random entries.
-    c = synth.e5m2_config_case()
+    # same kernels), and the varlen prefill with int8 packed keys and their
+    # scales: stratified full rows and random entries.
+    c = synth.e5m2_config_case() if which == "e5m2" else synth.i8_prefill_config_case()
     log(f"[gpu] config {c.name}")
     got = run_gpu(c, dev)
     pts, nrows = _sample_points(c, got.shape, 256, 10000, 555)
