@@ -166,12 +166,13 @@ def long_context_case():
                            layout="BBND", init_blocks=1, local_blocks=2)
 
 
-def long_prefill_case():
+def long_prefill_case(qdtype: str = "bf16"):
     """A prefill of 6144 tokens at the end of a 1,048,576-key context (its
     rows span 8192 blocks, the causal diagonal at the last 48) and one of 100
-    tokens over 200,000 keys; 8 heads over one KV head, bf16 packed keys
-    (320 MB), output 8 x 6244 x 8192 float32 (1.6 GB)."""
+    tokens over 200,000 keys; 8 heads over one KV head, bf16 (320 MB) or
+    MXFP4 (80 MB and scales) packed keys, output 8 x 6244 x 8192 float32
+    (1.6 GB)."""
     import synth
-    return synth.make_case("long_prefill_tnd_bf16", 8500, q_lens=[6144, 100],
-                           kv_lens=[1 << 20, 200_000], Hq=8, Hkv=1, qdtype="bf16",
-                           layout="TND", init_blocks=1, local_blocks=2)
+    return synth.make_case(f"long_prefill_tnd_{qdtype}", 8500 if qdtype == "bf16" else 8501,
+                           q_lens=[6144, 100], kv_lens=[1 << 20, 200_000], Hq=8, Hkv=1,
+                           qdtype=qdtype, layout="TND", init_blocks=1, local_blocks=2)

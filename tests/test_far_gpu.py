@@ -15,7 +15,7 @@ kernel families:
 * two requests past a million keys (a decode token and a speculative step),
   compared whole, with the top-k selection on their ~12k-block rows;
 * a 6144-token prefill at the end of a million-key context (8192-block rows),
-  compared on stratified whole rows.
+  bf16 and MXFP4, compared on stratified whole rows.
 
 The far inputs are the small cases of tests/far.py placed so that the result
 is unchanged (checked with the oracle on the CPU in test_far_cpu.py), so the
@@ -184,11 +184,19 @@ def test_long_context_and_topk(family, dev, long_ctx):
     assert bad == 0 and differ <= 2
 
 
+_LONG = {}
+
+
 @pytest.mark.parametrize("family", [0, 1])
-def test_long_prefill(family, dev):
+@pytest.mark.parametrize("qdtype", ["bf16", "mxfp4"])
+def test_long_prefill(qdtype, family, dev):
     from test_parity_gpu import assert_rows_match, gpu_rows, oracle_rows, run_gpu
-    case = far.long_prefill_case()
-    log(f"[gpu] long prefill family={family}: q {case.T} tokens, kv_len {case.kv_len.tolist()}")
+    if qdtype not in _LONG:
+        _LONG.clear()                              # one case's inputs held at a time
+        _LONG[qdtype] = far.long_prefill_case(qdtype)
+    case = _LONG[qdtype]
+    log(f"[gpu] long prefill {qdtype} family={family}: q {case.T} tokens, "
+        f"kv_len {case.kv_len.tolist()}")
     rows, ref = oracle_rows(case, 64, 8501)      # cached for the second family
     got = gpu_rows(run_gpu(case, dev, family), rows)
     assert_rows_match(ref, got, tol_of(case), f"long prefill family={family}")
